@@ -1,0 +1,244 @@
+"""Throughput of the MapFlow hot path on one MI355X.
+
+A step is one pass of the whole path over one batch that is already resident
+in HBM: block statistics (one launch over all layers), selection + scan +
+extraction (the staged compression), and the fused mapped attention . V
+(one launch over all receiver layers).  Default workload: bf16, one 8192-token
+causal sequence, 16 mapped layers, sender 32 heads -> receiver 24 heads,
+d = 128, B = 64, tau = 0.95 (the pages' 8B -> 3B class pair at 8K context).
+
+Prints one JSON line.  `value` is whole-step throughput in tokens/s; the
+per-kernel figures (fused kernel GB/s and fraction of HBM peak, compression
+tokens/s, stats TFLOP/s) and the roofline of the dominant kernel sit beside
+it, together with the CPU oracle timed on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = {
+    "block_stats_kernel": "cross_model_attention_mf_amd/csrc/k_stats.hip",
+    "mapped": "cross_model_attention_mf_amd/csrc/k_mapped.hip",
+    "extract_kernel": "cross_model_attention_mf_amd/csrc/k_compress.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tau", type=float, default=0.95)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rowblocks", type=int, default=6)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counters, or None when the
+    kernel's source has changed since they were taken."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = c.get(kernel)
+    if not e or e.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, tau, n_rowblocks, layers):
+    """The oracle (as is) on a bounded sample: every sender head of a few
+    row-blocks spread over one layer (stats, selection, extraction), then the
+    mapped output of those row-blocks; extrapolated by causal-pair count to
+    the whole step."""
+    from threadpoolctl import threadpool_info
+
+    from cross_model_attention_mf_amd import synth
+    from oracle import mapflow_oracle as orc
+
+    li = synth.layer_inputs(wl, 0)
+    lay = synth.batch_layout(wl)
+    q, k, v = synth.to_f64(li.q), synth.to_f64(li.k), synth.to_f64(li.v)
+    W = li.w.double().numpy()
+    rbs = orc.enumerate_rowblocks(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    n = len(rbs)
+    pick = sorted({int(x) for x in np.linspace(0, n - 1, n_rowblocks)})
+    scale = orc.default_scale(wl.d)
+    t0 = time.perf_counter()
+    for i in pick:
+        rb = rbs[i]
+        kv = []
+        for h in range(wl.H_s):
+            u = orc.compress_unit(q, k, rb, h, wl.B, tau, scale)
+            kv.append((u.sel.kept, u.values))
+        orc.mapped_rowblock(kv, W, v, rb, wl.B)
+    dt = time.perf_counter() - t0
+    pairs = lambda rb: rb.rows * (rb.last_pos + 1)
+    frac = sum(pairs(rbs[i]) for i in pick) / sum(pairs(rb) for rb in rbs)
+    step_s = dt / frac * layers
+    threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+    return {"value": round(lay.total_q / step_s, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"layer 0, {len(pick)} of {n} row-blocks x all {wl.H_s} sender heads "
+                      f"(stats, selection, extraction, mapped output); {dt:.1f} s measured, "
+                      f"extrapolated by causal pairs to {layers} layers"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+
+    if not os.path.exists(mf.LIB_PATH):
+        from cross_model_attention_mf_amd import build_lib
+        build_lib.build()
+    dev = torch.device("cuda")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}))
+        return
+
+    wl = synth.workload_by_id(3).replace(num_layers=args.layers)
+    tau = args.tau
+    L = wl.num_layers
+    print(f"[bench] generating {L} layers of {wl.name}", file=sys.stderr, flush=True)
+    lay = synth.batch_layout(wl)
+    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(L)]
+    q = torch.stack([x.q for x in ins]).to(dev)
+    k = torch.stack([x.k for x in ins]).to(dev)
+    v = torch.stack([x.v for x in ins]).to(dev)
+    W = torch.stack([x.w for x in ins]).to(dev)
+    del ins
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    cap = pipeline.count_capacity(batch, q, k, wl.B, tau)
+    st = pipeline.alloc_sender(batch, q, k, wl.B, cap)
+    out = torch.empty((L, lay.total_q, wl.H_r, wl.d), dtype=torch.bfloat16, device=dev)
+    lmap = list(range(L))
+    desc_r = mf.receiver_desc(v, wl.H_s, wl.H_r, wl.d, wl.B, lmap, L, out[0].numel(), st.col_idx.numel())
+    stream = torch.cuda.current_stream()
+    print(f"[bench] nnz={cap} blocks ({cap * wl.B * wl.B * 2 / 1e9:.2f} GB of values)", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass)
+        if ev is not None:
+            ev[1].record(stream)
+        mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, tau, st.row_ptr,
+                           st.col_idx, st.values, cap, st.workspace, sync_count=False)
+        if ev is not None:
+            ev[2].record(stream)
+        mf.mapped_attn_v(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_stats = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_comp = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_map = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+    assert int(st.row_ptr[-1]) == cap
+
+    N = lay.total_q
+    # algorithmic work (see the design notes): one causal Q K^T for the stats;
+    # kept values + row_ptr + col_idx + V once + W + O once for the fused kernel
+    stats_flops = L * wl.H_s * N * (N + 1) / 2 * 2 * wl.d
+    nrows = L * wl.H_s * batch.total_rowblocks
+    map_bytes = (cap * wl.B * wl.B * 2 + (nrows + 1) * 4 + cap * 4 + L * N * wl.hkv_r * wl.d * 2
+                 + L * wl.H_r * wl.H_s * 4 + L * N * wl.H_r * wl.d * 2)
+    stats_tflops = stats_flops / t_stats / 1e12
+    map_gbs = map_bytes / t_map / 1e9
+    rooflines = {
+        "block_stats_kernel": {"bound": "mfma", "achieved": round(stats_tflops, 2),
+                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(stats_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "traffic": measured_traffic("block_stats_kernel"),
+                               "us_per_launch": round(t_stats * 1e6, 1)},
+        "mapped": {"bound": "hbm", "achieved": round(map_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(map_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic("mapped"),
+                   "us_per_launch": round(t_map * 1e6, 1)},
+    }
+    dominant = max(("block_stats_kernel", t_stats), ("mapped", t_map), key=lambda x: x[1])[0]
+    res = {
+        "metric": "mapped-attn·V GB/s & % HBM peak; block-compress tokens/s at 8K ctx",
+        "value": round(N / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 causal 8192 tokens, 16 mapped layers, sender 32 heads -> "
+                               "receiver 24 heads, d=128, B=64, structured Q/K",
+                   "seq_len": N, "layers": L, "tau": tau, "B": wl.B, "H_s": wl.H_s,
+                   "H_r": wl.H_r, "d": wl.d},
+        "mapped_attn_v": {"GB_per_s": round(map_gbs, 1), "hbm_frac": round(map_gbs / HBM_PEAK_GBS, 4),
+                          "us_per_layer": round(t_map / L * 1e6, 1),
+                          "tokens_per_s": round(N * L / t_map, 1)},
+        "block_compress": {"tokens_per_s": round(N / (t_stats + t_comp), 1),
+                           "us_per_layer": round((t_stats + t_comp) / L * 1e6, 1),
+                           "stats_us_per_layer": round(t_stats / L * 1e6, 1),
+                           "select_extract_us_per_layer": round(t_comp / L * 1e6, 1)},
+        "kept_blocks": cap,
+        "kept_fraction": round(cap / (L * wl.H_s * sum(i + 1 for i in range(batch.total_rowblocks))), 4),
+        "roofline": {k_: v_ for k_, v_ in rooflines[dominant].items() if k_ != "us_per_launch"},
+        "roofline_kernel": dominant,
+        "rooflines": rooflines,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, tau, args.cpu_sample_rowblocks, L)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,251 @@
+// C-ABI entry points: validate every argument on the host, then launch the
+// gfx950 kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "errors.h"
+#include "internal.h"
+#include "mapflow.h"
+
+using mf::fail;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+mf_status hip_fail(int err, const char* what) {
+  return fail(MF_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+mf_status check_batch(const mf_batch* b, int B, const char* fn) {
+  if (!b) return fail(MF_ERR_INVALID, "%s: batch is NULL", fn);
+  const mf_plan_info& in = b->info;
+  if (in.block != B) return fail(MF_ERR_INVALID, "%s: batch planned for B = %d, call uses B = %d", fn, in.block, B);
+  if (in.num_seqs < 0 || in.total_rowblocks < 0 || in.max_colblocks < 0 || in.total_q < 0 || in.total_k < 0)
+    return fail(MF_ERR_INVALID, "%s: negative size in batch info", fn);
+  if (in.plan_len != in.num_seqs + 1 + in.total_rowblocks)
+    return fail(MF_ERR_INVALID, "%s: batch info is inconsistent (plan_len)", fn);
+  if (in.max_k_len > MF_MAX_KEYS) return fail(MF_ERR_UNSUPPORTED, "%s: %d keys > MF_MAX_KEYS", fn, in.max_k_len);
+  if (in.total_rowblocks > 0 && (!b->cu_seqlens_q || !b->cu_seqlens_k || !b->plan))
+    return fail(MF_ERR_INVALID, "%s: batch device arrays are NULL", fn);
+  return MF_OK;
+}
+
+mf_status check_common(mf_dtype dt, int L, int H, int Hkv, int d, int B, const char* fn) {
+  if (dt != MF_F32 && dt != MF_BF16) return fail(MF_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (L < 0) return fail(MF_ERR_INVALID, "%s: num_layers = %d < 0", fn, L);
+  if (B != 32 && B != 64 && B != 128) return fail(MF_ERR_UNSUPPORTED, "%s: B = %d not in {32, 64, 128}", fn, B);
+  if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "%s: d = %d not in {64, 128}", fn, d);
+  if (H < 1 || H > 64) return fail(MF_ERR_UNSUPPORTED, "%s: %d heads not in [1, 64]", fn, H);
+  if (Hkv < 1 || H % Hkv) return fail(MF_ERR_INVALID, "%s: %d kv heads do not divide %d heads", fn, Hkv, H);
+  return MF_OK;
+}
+
+mf_status check_sender(const mf_sender_desc* s, const mf_batch* b, const char* fn) {
+  if (!s) return fail(MF_ERR_INVALID, "%s: desc is NULL", fn);
+  mf_status st = check_common(s->dtype, s->num_layers, s->H_s, s->H_kv_s, s->d, s->B, fn);
+  if (st) return st;
+  st = check_batch(b, s->B, fn);
+  if (st) return st;
+  if (!(s->sm_scale >= 0.f) || isinf(s->sm_scale)) return fail(MF_ERR_INVALID, "%s: sm_scale must be finite and >= 0", fn);
+  if (s->num_layers > 1) {
+    if (s->layer_stride_q < (int64_t)b->info.total_q * s->H_s * s->d ||
+        s->layer_stride_k < (int64_t)b->info.total_k * s->H_kv_s * s->d)
+      return fail(MF_ERR_INVALID, "%s: layer strides smaller than one layer", fn);
+  }
+  return MF_OK;
+}
+
+mf::BatchArgs batch_args(const mf_batch* b) {
+  mf::BatchArgs a;
+  a.cu_q = b->cu_seqlens_q;
+  a.cu_k = b->cu_seqlens_k;
+  a.q_pos0 = b->q_pos0;
+  a.plan = b->plan;
+  a.num_seqs = b->info.num_seqs;
+  a.total_rb = b->info.total_rowblocks;
+  a.max_cb = b->info.max_colblocks;
+  a.total_q = b->info.total_q;
+  a.total_k = b->info.total_k;
+  return a;
+}
+
+double scale_of(const mf_sender_desc* s) { return s->sm_scale > 0.f ? (double)s->sm_scale : 1.0 / sqrt((double)s->d); }
+
+size_t device_lds_limit() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 65536;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 65536;
+  return (size_t)v;
+}
+
+struct WorkspaceLayout {
+  size_t counts, bits, total, bytes;
+  int words;
+};
+
+WorkspaceLayout workspace_layout(const mf_sender_desc* s, const mf_batch* b) {
+  WorkspaceLayout w;
+  const size_t nrows = (size_t)s->num_layers * s->H_s * b->info.total_rowblocks;
+  w.words = (b->info.max_colblocks + 31) / 32;
+  w.counts = 0;
+  w.bits = align256(nrows * 4);
+  w.total = w.bits + align256(nrows * (size_t)w.words * 4);
+  w.bytes = w.total + 256;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mf_status_string(mf_status s) {
+  switch (s) {
+    case MF_OK: return "MF_OK";
+    case MF_ERR_INVALID: return "MF_ERR_INVALID";
+    case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED";
+    case MF_ERR_CAPACITY: return "MF_ERR_CAPACITY";
+    case MF_ERR_HIP: return "MF_ERR_HIP";
+    case MF_ERR_WORKSPACE: return "MF_ERR_WORKSPACE";
+  }
+  return "MF_ERR_UNKNOWN";
+}
+
+const char* mf_last_error_message(void) { return mf::error_buffer(); }
+
+const char* mf_version(void) { return "mapflow-mi355x 0.1"; }
+
+mf_status mf_block_stats(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
+                         float* row_lse, float* block_mass, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_block_stats";
+  mf_status st = check_sender(desc, batch, fn);
+  if (st) return st;
+  if (desc->num_layers == 0 || batch->info.total_rowblocks == 0) return MF_OK;
+  if (!q || !k || !row_lse || !block_mass) return fail(MF_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  const size_t lds = mf::block_stats_lds_bytes(desc->B, batch->info.max_colblocks);
+  if (lds > device_lds_limit())
+    return fail(MF_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed, device allows %zu", fn, lds, device_lds_limit());
+  mf::StatsArgs a;
+  a.b = batch_args(batch);
+  a.q = q; a.k = k; a.row_lse = row_lse; a.block_mass = block_mass;
+  a.lsq = desc->layer_stride_q; a.lsk = desc->layer_stride_k;
+  a.L = desc->num_layers; a.H = desc->H_s; a.Hkv = desc->H_kv_s; a.d = desc->d; a.B = desc->B;
+  a.scale = scale_of(desc);
+  const int e = mf::launch_block_stats(a, desc->dtype, stream);
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+size_t mf_compress_workspace_size(const mf_sender_desc* desc, const mf_batch* batch) {
+  if (!desc || !batch) return 0;
+  return workspace_layout(desc, batch).bytes;
+}
+
+mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
+                             const float* row_lse, const float* block_mass, float tau, int32_t* row_ptr,
+                             int32_t* col_idx, void* values, int64_t capacity_blocks, int64_t* nnz_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_compress_blocks";
+  mf_status st = check_sender(desc, batch, fn);
+  if (st) return st;
+  if (!(tau > 0.f && tau <= 1.f)) return fail(MF_ERR_INVALID, "%s: tau = %g not in (0, 1]", fn, (double)tau);
+  if (capacity_blocks < 0) return fail(MF_ERR_INVALID, "%s: capacity_blocks < 0", fn);
+  if (!row_ptr) return fail(MF_ERR_INVALID, "%s: row_ptr is NULL", fn);
+  if (capacity_blocks > 0 && !col_idx) return fail(MF_ERR_INVALID, "%s: col_idx is NULL", fn);
+  const int64_t nrows = (int64_t)desc->num_layers * desc->H_s * batch->info.total_rowblocks;
+  if (nrows > INT32_MAX - 1) return fail(MF_ERR_UNSUPPORTED, "%s: too many CSR rows", fn);
+  if (nrows > 0 && (!q || !k || !row_lse || !block_mass)) return fail(MF_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  const WorkspaceLayout wl = workspace_layout(desc, batch);
+  if (!workspace || workspace_bytes < wl.bytes)
+    return fail(MF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, wl.bytes, workspace_bytes);
+  if (mf::select_lds_bytes(batch->info.max_colblocks) > device_lds_limit())
+    return fail(MF_ERR_UNSUPPORTED, "%s: too many column blocks for the selection sort", fn);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + wl.counts);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + wl.bits);
+  long long* total = reinterpret_cast<long long*>(ws + wl.total);
+  const mf::BatchArgs ba = batch_args(batch);
+
+  if (nrows > 0) {
+    mf::SelectArgs s;
+    s.b = ba; s.block_mass = block_mass; s.counts = counts; s.keep_bits = bits; s.words = wl.words;
+    s.L = desc->num_layers; s.H = desc->H_s; s.B = desc->B; s.tau = (double)tau;
+    int e = mf::launch_select(s, stream);
+    if (e) return hip_fail(e, fn);
+  }
+  mf::ScanArgs sc;
+  sc.counts = counts; sc.row_ptr = row_ptr; sc.total = total; sc.n = nrows;
+  int e = mf::launch_scan(sc, stream);
+  if (e) return hip_fail(e, fn);
+  if (nnz_out) {
+    long long nnz = 0;
+    e = (int)hipMemcpyAsync(&nnz, total, sizeof(nnz), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (!e) e = (int)hipStreamSynchronize((hipStream_t)stream);
+    if (e) return hip_fail(e, fn);
+    *nnz_out = nnz;
+    if (capacity_blocks == 0 && !col_idx) return MF_OK;  // count only
+    if (nnz > capacity_blocks)
+      return fail(MF_ERR_CAPACITY, "%s: %lld kept blocks exceed capacity %lld", fn, nnz, (long long)capacity_blocks);
+  }
+  if (nrows == 0 || capacity_blocks == 0) return MF_OK;
+  mf::ExtractArgs x;
+  x.b = ba; x.q = q; x.k = k; x.row_lse = row_lse; x.row_ptr = row_ptr; x.keep_bits = bits; x.words = wl.words;
+  x.col_idx = col_idx; x.values = values; x.capacity = capacity_blocks;
+  x.lsq = desc->layer_stride_q; x.lsk = desc->layer_stride_k;
+  x.L = desc->num_layers; x.H = desc->H_s; x.Hkv = desc->H_kv_s; x.d = desc->d; x.B = desc->B;
+  x.scale = scale_of(desc);
+  e = mf::launch_extract(x, desc->dtype, stream);
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
+                           const int32_t* col_idx, const void* values, const float* W, const void* v, void* o,
+                           void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_mapped_attn_v";
+  if (!desc) return fail(MF_ERR_INVALID, "%s: desc is NULL", fn);
+  mf_status st = check_common(desc->dtype, desc->num_layers, desc->H_r, desc->H_kv_r, desc->d, desc->B, fn);
+  if (st) return st;
+  st = check_batch(batch, desc->B, fn);
+  if (st) return st;
+  if (desc->H_s < 1 || desc->H_s > 64) return fail(MF_ERR_UNSUPPORTED, "%s: H_s = %d not in [1, 64]", fn, desc->H_s);
+  if (desc->num_layers > MF_MAX_LAYERS) return fail(MF_ERR_UNSUPPORTED, "%s: more than %d layers", fn, MF_MAX_LAYERS);
+  if (desc->sender_layers < 1 && desc->num_layers > 0) return fail(MF_ERR_INVALID, "%s: sender_layers < 1", fn);
+  if (desc->num_layers > 0 && !desc->layer_map) return fail(MF_ERR_INVALID, "%s: layer_map is NULL", fn);
+  for (int l = 0; l < desc->num_layers; ++l)
+    if (desc->layer_map[l] < 0 || desc->layer_map[l] >= desc->sender_layers)
+      return fail(MF_ERR_INVALID, "%s: layer_map[%d] = %d outside [0, %d)", fn, l, desc->layer_map[l], desc->sender_layers);
+  if (desc->block_table) {
+    if (desc->page_size < 1 || desc->max_pages < 1 || desc->num_pages < 1)
+      return fail(MF_ERR_INVALID, "%s: paged values need page_size, max_pages, num_pages >= 1", fn);
+    if ((int64_t)desc->max_pages * desc->page_size < batch->info.max_k_len)
+      return fail(MF_ERR_INVALID, "%s: max_pages * page_size < longest key range", fn);
+  }
+  if (desc->num_layers > 1) {
+    const int64_t vrows = desc->block_table ? desc->num_pages * desc->page_size : (int64_t)batch->info.total_k;
+    if (desc->layer_stride_v < vrows * desc->H_kv_r * desc->d ||
+        desc->layer_stride_o < (int64_t)batch->info.total_q * desc->H_r * desc->d)
+      return fail(MF_ERR_INVALID, "%s: layer strides smaller than one layer", fn);
+  }
+  if (desc->csr_capacity < 0) return fail(MF_ERR_INVALID, "%s: csr_capacity < 0", fn);
+  if (desc->num_layers == 0 || batch->info.total_rowblocks == 0) return MF_OK;
+  if (!row_ptr || !W || !v || !o || (desc->csr_capacity > 0 && (!col_idx || !values)))
+    return fail(MF_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  mf::MappedArgs a;
+  memset(&a, 0, sizeof(a));
+  a.b = batch_args(batch);
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.values = values; a.W = W; a.v = v; a.o = o;
+  a.lsv = desc->layer_stride_v; a.lso = desc->layer_stride_o;
+  a.block_table = desc->block_table; a.page_size = desc->page_size; a.max_pages = desc->max_pages;
+  a.num_pages = desc->num_pages; a.csr_capacity = desc->csr_capacity;
+  a.L = desc->num_layers; a.Ls = desc->sender_layers; a.Hs = desc->H_s; a.Hr = desc->H_r; a.Hkv = desc->H_kv_r;
+  a.d = desc->d; a.B = desc->B;
+  for (int l = 0; l < desc->num_layers; ++l) a.layer_map[l] = desc->layer_map[l];
+  const int e = mf::launch_mapped(a, desc->dtype, stream);
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mapflow.h"
+
+namespace mf {
+
+// Fields of a packed batch every kernel needs.
+struct BatchArgs {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* q_pos0;   // may be null
+  const int32_t* plan;
+  int32_t num_seqs;
+  int32_t total_rb;
+  int32_t max_cb;
+  int32_t total_q;
+  int32_t total_k;
+};
+
+struct StatsArgs {
+  BatchArgs b;
+  const void* q;
+  const void* k;
+  float* row_lse;
+  float* block_mass;
+  int64_t lsq, lsk;        // layer strides (elements)
+  int32_t L, H, Hkv, d, B;
+  double scale;            // logit scale
+};
+
+struct SelectArgs {
+  BatchArgs b;
+  const float* block_mass;
+  int32_t* counts;         // [L*H*total_rb]
+  uint32_t* keep_bits;     // [L*H*total_rb][words]
+  int32_t words;
+  int32_t L, H, B;
+  double tau;
+};
+
+struct ScanArgs {
+  const int32_t* counts;
+  int32_t* row_ptr;
+  long long* total;        // device int64
+  int64_t n;
+};
+
+struct ExtractArgs {
+  BatchArgs b;
+  const void* q;
+  const void* k;
+  const float* row_lse;
+  const int32_t* row_ptr;
+  const uint32_t* keep_bits;
+  int32_t words;
+  int32_t* col_idx;
+  void* values;            // may be null
+  int64_t capacity;
+  int64_t lsq, lsk;
+  int32_t L, H, Hkv, d, B;
+  double scale;
+};
+
+struct MappedArgs {
+  BatchArgs b;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* values;
+  const float* W;
+  const void* v;
+  void* o;
+  int64_t lsv, lso;
+  const int32_t* block_table;
+  int32_t page_size, max_pages;
+  int64_t num_pages;
+  int64_t csr_capacity;
+  int32_t L, Ls, Hs, Hr, Hkv, d, B;
+  int32_t layer_map[MF_MAX_LAYERS];
+};
+
+// Launchers: return 0 on success, a hipError_t value otherwise.
+int launch_block_stats(const StatsArgs& a, mf_dtype dt, void* stream);
+size_t block_stats_lds_bytes(int B, int max_cb);
+int launch_select(const SelectArgs& a, void* stream);
+int launch_scan(const ScanArgs& a, void* stream);
+int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream);
+int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream);
+size_t select_lds_bytes(int max_cb);
+
+}  // namespace mf

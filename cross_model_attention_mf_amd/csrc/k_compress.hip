@@ -1,0 +1,265 @@
+// Stage 2 of the staged block compression: keep, per (layer, sender head,
+// row-block), the blocks needed to reach cumulative attention probability
+// tau, then extract their probabilities (MapFlow page, section
+// "让复用真正省时…", paragraph "第一").
+//
+//   select:  one workgroup per CSR row.  Keys (mass desc, column asc) are
+//            bitonic-sorted in LDS; the sorted masses are prefix-summed in
+//            fp64; the cut is the first prefix reaching tau.  Output: kept
+//            count and a bitmask over column blocks.
+//   scan:    one workgroup turns the counts into row_ptr (exclusive scan).
+//   extract: one workgroup per CSR row recomputes S = Q K^T for its kept
+//            blocks only (MFMA), P = exp(S * scale - row_lse), and writes
+//            B x B values row-major through an LDS transpose so every store
+//            is a full 16-byte vector.
+#include "device_common.h"
+#include "internal.h"
+
+namespace mf {
+
+namespace {
+
+constexpr int kSelThreads = 256;
+
+__global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a, int n2) {
+  extern __shared__ __align__(16) char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);                 // [n2]
+  double* tsum = reinterpret_cast<double*>(keys + n2);                // [kSelThreads]
+  uint32_t* bits = reinterpret_cast<uint32_t*>(tsum + kSelThreads);   // [words]
+  __shared__ int kstar_s;
+
+  const int rb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, a.B, rb);
+  const size_t row = ((size_t)l * a.H + h) * a.b.total_rb + rb;
+  const float* __restrict__ m = a.block_mass + row * (size_t)a.b.max_cb;
+  const int n = ri.ncand;
+  const int tid = threadIdx.x;
+
+  for (int t = tid; t < n2; t += kSelThreads) {
+    uint64_t key = ~0ull;
+    if (t < n) key = ((uint64_t)(0xFFFFFFFFu - __float_as_uint(m[t])) << 32) | (uint32_t)t;
+    keys[t] = key;
+  }
+  for (int t = tid; t < a.words; t += kSelThreads) bits[t] = 0u;
+  if (tid == 0) kstar_s = n;
+  __syncthreads();
+
+  // bitonic sort, ascending keys = mass descending, column ascending
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int t = tid; t < n2; t += kSelThreads) {
+        const int p = t ^ jj;
+        if (p > t) {
+          const uint64_t x = keys[t], y = keys[p];
+          const bool up = (t & k) == 0;
+          if ((x > y) == up) { keys[t] = y; keys[p] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // fp64 prefix sums of the sorted masses: contiguous chunk per thread
+  const int per = (n2 + kSelThreads - 1) / kSelThreads;
+  const int t0 = tid * per;
+  double local = 0.0;
+  for (int t = t0; t < min(t0 + per, n); ++t)
+    local += (double)__uint_as_float(0xFFFFFFFFu - (uint32_t)(keys[t] >> 32));
+  tsum[tid] = local;
+  __syncthreads();
+  if (a.tau < 1.0) {
+    double before = 0.0;
+    for (int u = 0; u < tid; ++u) before += tsum[u];
+    double c = before;
+    for (int t = t0; t < min(t0 + per, n); ++t) {
+      c += (double)__uint_as_float(0xFFFFFFFFu - (uint32_t)(keys[t] >> 32));
+      if (c >= a.tau) { atomicMin(&kstar_s, t + 1); break; }
+    }
+  }
+  __syncthreads();
+  const int kstar = kstar_s;
+  for (int t = tid; t < kstar; t += kSelThreads) {
+    const uint32_t j = (uint32_t)(keys[t] & 0xFFFFFFFFu);
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  uint32_t* __restrict__ out = a.keep_bits + row * (size_t)a.words;
+  for (int t = tid; t < a.words; t += kSelThreads) out[t] = bits[t];
+  if (tid == 0) a.counts[row] = kstar;
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
+  __shared__ long long wsum[kScanThreads / 64];
+  __shared__ long long carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < a.n; base += kScanThreads) {
+    const int64_t i = base + tid;
+    const long long x = i < a.n ? a.counts[i] : 0;
+    // inclusive scan inside the wave
+    long long v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(v, off, 64);
+      if (lane >= off) v += y;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    long long pre = 0;
+    for (int u = 0; u < w; ++u) pre += wsum[u];
+    const long long carry = carry_s;
+    if (i < a.n) a.row_ptr[i] = (int32_t)(carry + pre + v - x);
+    __syncthreads();
+    if (tid == kScanThreads - 1) carry_s = carry + pre + v;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.row_ptr[a.n] = (int32_t)carry_s;
+    *a.total = carry_s;
+  }
+}
+
+template <typename T, int B, int D>
+__global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
+  constexpr int NT = B / 16;
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte store
+  constexpr int PITCH = B + VEC;               // LDS row pitch (elements)
+  __shared__ __align__(16) T tile[B / 16][16 * PITCH];
+
+  const int rb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
+  const size_t lh = (size_t)l * a.H + h;
+  const size_t row = lh * a.b.total_rb + rb;
+  const int64_t base = a.row_ptr[row];
+  const int hk = h / (a.H / a.Hkv);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  const T* __restrict__ qbase = reinterpret_cast<const T*>(a.q) + (size_t)l * a.lsq;
+  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.k) + (size_t)l * a.lsk +
+                                (size_t)ri.k0 * a.Hkv * D + (size_t)hk * D;
+  const size_t kstride = (size_t)a.Hkv * D;
+  QFrag<T, D> qf;
+  {
+    const int r = min(16 * w + lr, ri.rows - 1);
+    qf.load(qbase + ((size_t)(ri.q0 + r) * a.H + h) * D, lane);
+  }
+  // exp(s - lse) with s = scale * S: scale split in two floats so the
+  // product keeps ~48 bits before the subtraction
+  const float s_hi = (float)a.scale;
+  const float s_lo = (float)(a.scale - (double)s_hi);
+  float lse[4];
+  int rowl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rowl[i] = 16 * w + 4 * lg + i;
+    lse[i] = rowl[i] < ri.rows ? a.row_lse[lh * a.b.total_q + ri.q0 + rowl[i]] : 0.f;
+  }
+  const uint32_t* __restrict__ kb = a.keep_bits + row * (size_t)a.words;
+  T* __restrict__ vals = reinterpret_cast<T*>(a.values);
+  T* __restrict__ my = tile[w];
+
+  int64_t e = base;
+  for (int wd = 0; wd < a.words; ++wd) {
+    uint32_t bitsw = kb[wd];
+    while (bitsw) {
+      const int j = wd * 32 + __builtin_ctz(bitsw);
+      bitsw &= bitsw - 1;
+      if (e < a.capacity) {
+        if (threadIdx.x == 0) a.col_idx[e] = j;
+        if (vals) {
+          f32x4 acc[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int c = min(j * B + 16 * nt + lr, ri.klen - 1);
+            acc[nt] = qf.dot(kbase + (size_t)c * kstride, lane, acc[nt]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = j * B + 16 * nt + lr;
+              float p = 0.f;
+              if (rowl[i] < ri.rows && c <= ri.pos0 + rowl[i]) {
+                float x = fmaf(acc[nt][i], s_hi, -lse[i]);
+                x = fmaf(acc[nt][i], s_lo, x);
+                p = exp2f(x * kLog2e);
+              }
+              my[(4 * lg + i) * PITCH + 16 * nt + lr] = from_f32<T>(p);
+            }
+          __syncthreads();
+          // 16 rows x B columns of this wave -> global, 16 bytes per lane store
+          T* __restrict__ dst = vals + (size_t)e * B * B + (size_t)(16 * w) * B;
+          constexpr int CH = 16 * B / VEC;
+          for (int c = lane; c < CH; c += 64) {
+            const int r = c / (B / VEC), col = (c % (B / VEC)) * VEC;
+            *reinterpret_cast<uint4*>(dst + (size_t)r * B + col) =
+                *reinterpret_cast<const uint4*>(my + r * PITCH + col);
+          }
+          __syncthreads();
+        }
+      }
+      ++e;
+    }
+  }
+}
+
+template <typename T, int B, int D>
+int launch_ex(const ExtractArgs& a, void* stream) {
+  dim3 grid(a.b.total_rb, a.H, a.L);
+  hipLaunchKernelGGL((extract_kernel<T, B, D>), grid, dim3(B * 4), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+template <typename T>
+int launch_ex_d(const ExtractArgs& a, void* stream) {
+  switch (a.B * 1000 + a.d) {
+    case 32064: return launch_ex<T, 32, 64>(a, stream);
+    case 32128: return launch_ex<T, 32, 128>(a, stream);
+    case 64064: return launch_ex<T, 64, 64>(a, stream);
+    case 64128: return launch_ex<T, 64, 128>(a, stream);
+    case 128064: return launch_ex<T, 128, 64>(a, stream);
+    case 128128: return launch_ex<T, 128, 128>(a, stream);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+size_t select_lds_bytes(int max_cb) {
+  const int n2 = next_pow2(max_cb < 1 ? 1 : max_cb);
+  return (size_t)n2 * 8 + kSelThreads * 8 + (size_t)((max_cb + 31) / 32) * 4;
+}
+
+int launch_select(const SelectArgs& a, void* stream) {
+  if (a.b.total_rb == 0 || a.L == 0) return 0;
+  const int n2 = next_pow2(a.b.max_cb < 1 ? 1 : a.b.max_cb);
+  const size_t lds = select_lds_bytes(a.b.max_cb);
+  hipError_t e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return (int)e;
+  dim3 grid(a.b.total_rb, a.H, a.L);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), lds, (hipStream_t)stream, a, n2);
+  return (int)hipGetLastError();
+}
+
+int launch_scan(const ScanArgs& a, void* stream) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream) {
+  if (a.b.total_rb == 0 || a.L == 0) return 0;
+  return dt == MF_BF16 ? launch_ex_d<bf16>(a, stream) : launch_ex_d<float>(a, stream);
+}
+
+}  // namespace mf

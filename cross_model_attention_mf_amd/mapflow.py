@@ -1,0 +1,223 @@
+"""ctypes binding of libmapflow.so (include/mapflow.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the library.  Torch tensors supply device memory and the current stream.
+The binding refuses to work without the built library: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmapflow.so")
+
+MF_OK, MF_ERR_INVALID, MF_ERR_UNSUPPORTED, MF_ERR_CAPACITY, MF_ERR_HIP, MF_ERR_WORKSPACE = range(6)
+MF_F32, MF_BF16 = 0, 1
+MF_MAX_KEYS = 40448
+MF_MAX_LAYERS = 256
+EXPORTS = ("mf_plan", "mf_block_stats", "mf_compress_workspace_size", "mf_compress_blocks",
+           "mf_mapped_attn_v", "mf_status_string", "mf_last_error_message", "mf_version")
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("total_rowblocks", ctypes.c_int32), ("max_colblocks", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32),
+                ("max_k_len", ctypes.c_int32), ("plan_len", ctypes.c_int32)]
+
+
+class BatchC(ctypes.Structure):
+    _fields_ = [("info", PlanInfo), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_k", ctypes.c_void_p), ("q_pos0", ctypes.c_void_p),
+                ("plan", ctypes.c_void_p)]
+
+
+class SenderDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("num_layers", ctypes.c_int32),
+                ("H_s", ctypes.c_int32), ("H_kv_s", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("B", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("layer_stride_q", ctypes.c_int64), ("layer_stride_k", ctypes.c_int64)]
+
+
+class ReceiverDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("num_layers", ctypes.c_int32),
+                ("sender_layers", ctypes.c_int32), ("layer_map", _i32p),
+                ("H_s", ctypes.c_int32), ("H_r", ctypes.c_int32), ("H_kv_r", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("layer_stride_v", ctypes.c_int64), ("layer_stride_o", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+                ("csr_capacity", ctypes.c_int64)]
+
+
+class MapflowError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def _status_name(s: int) -> str:
+    names = ["MF_OK", "MF_ERR_INVALID", "MF_ERR_UNSUPPORTED", "MF_ERR_CAPACITY", "MF_ERR_HIP", "MF_ERR_WORKSPACE"]
+    return names[s] if 0 <= s < len(names) else f"status {s}"
+
+
+def lib():
+    """Load libmapflow.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m cross_model_attention_mf_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.mf_plan.argtypes = [_i32p, _i32p, _i32p, i32, i32, _i32p, i64, ctypes.POINTER(PlanInfo)]
+    L.mf_block_stats.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp, vp]
+    L.mf_compress_workspace_size.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC)]
+    L.mf_compress_workspace_size.restype = sz
+    L.mf_compress_blocks.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
+                                     ctypes.c_float, vp, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
+    L.mf_mapped_attn_v.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
+                                   vp, vp, vp]
+    for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v"):
+        getattr(L, f).restype = ctypes.c_int
+    L.mf_status_string.argtypes = [ctypes.c_int]
+    L.mf_status_string.restype = ctypes.c_char_p
+    L.mf_last_error_message.restype = ctypes.c_char_p
+    L.mf_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != MF_OK:
+        raise MapflowError(status, lib().mf_last_error_message().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MF_BF16
+    if t == torch.float32:
+        return MF_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _as_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def plan(cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int],
+         q_pos0: Optional[Sequence[int]], B: int):
+    """mf_plan on host arrays -> (PlanInfo, int32 plan array)."""
+    L = lib()
+    cq, ck = _as_i32(cu_seqlens_q), _as_i32(cu_seqlens_k)
+    p0 = None if q_pos0 is None else _as_i32(q_pos0)
+    ns = cq.shape[0] - 1
+    info = PlanInfo()
+    args = (cq.ctypes.data_as(_i32p), ck.ctypes.data_as(_i32p),
+            None if p0 is None else p0.ctypes.data_as(_i32p), ns, B)
+    st = L.mf_plan(*args, None, 0, ctypes.byref(info))
+    if st not in (MF_OK, MF_ERR_CAPACITY):
+        _check(st)
+    buf = np.zeros(max(info.plan_len, 1), dtype=np.int32)
+    _check(L.mf_plan(*args, buf.ctypes.data_as(_i32p), buf.shape[0], ctypes.byref(info)))
+    return info, buf[: info.plan_len]
+
+
+class Batch:
+    """A packed batch on the device: cu_seqlens, chunk starts and the plan."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, q_pos0, B: int, device="cuda"):
+        self.info, h_plan = plan(cu_seqlens_q, cu_seqlens_k, q_pos0, B)
+        self.B = B
+        self.cu_q = torch.from_numpy(_as_i32(cu_seqlens_q)).to(device)
+        self.cu_k = torch.from_numpy(_as_i32(cu_seqlens_k)).to(device)
+        self.q_pos0 = None if q_pos0 is None else torch.from_numpy(_as_i32(q_pos0)).to(device)
+        self.plan = torch.from_numpy(h_plan.copy() if h_plan.size else np.zeros(1, np.int32)).to(device)
+        self.c = BatchC(self.info, _ptr(self.cu_q), _ptr(self.cu_k), _ptr(self.q_pos0), _ptr(self.plan))
+
+    @property
+    def total_rowblocks(self) -> int:
+        return self.info.total_rowblocks
+
+    @property
+    def max_colblocks(self) -> int:
+        return self.info.max_colblocks
+
+
+def sender_desc(q: torch.Tensor, k: torch.Tensor, B: int, sm_scale: float = 0.0) -> SenderDesc:
+    """q [L, Tq, H, d] (or [Tq, H, d]), k [L, Tk, H_kv, d]; contiguous."""
+    if q.dim() == 3:
+        q, k = q[None], k[None]
+    L_, _, H, d = q.shape
+    return SenderDesc(dtype_code(q.dtype), L_, H, k.shape[2], d, B, sm_scale,
+                      q[0].numel(), k[0].numel())
+
+
+def block_stats(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, stream=None):
+    _check(lib().mf_block_stats(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(q), _ptr(k),
+                                _ptr(row_lse), _ptr(block_mass), _stream(stream)))
+
+
+def compress_workspace_size(desc: SenderDesc, batch: Batch) -> int:
+    return int(lib().mf_compress_workspace_size(ctypes.byref(desc), ctypes.byref(batch.c)))
+
+
+def compress_blocks(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, tau: float,
+                    row_ptr, col_idx, values, capacity: int, workspace, sync_count: bool = True,
+                    stream=None) -> Optional[int]:
+    """Returns the kept-block count when sync_count (one stream sync), else None."""
+    nnz = ctypes.c_int64(-1)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().mf_compress_blocks(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(q), _ptr(k),
+                                  _ptr(row_lse), _ptr(block_mass), float(tau), _ptr(row_ptr),
+                                  _ptr(col_idx), _ptr(values), int(capacity),
+                                  ctypes.byref(nnz) if sync_count else None, _ptr(workspace),
+                                  ws_bytes, _stream(stream))
+    _check(st)
+    return int(nnz.value) if sync_count else None
+
+
+def receiver_desc(v: torch.Tensor, H_s: int, H_r: int, d: int, B: int, layer_map: Sequence[int],
+                  sender_layers: int, o_layer_stride: int, csr_capacity: int, block_table=None,
+                  page_size: int = 0, v_layer_stride: Optional[int] = None):
+    """v: [L, Tk, H_kv_r, d] packed or [L, pages, page_size, H_kv_r, d] paged."""
+    lm = _as_i32(layer_map)
+    paged = block_table is not None
+    H_kv_r = v.shape[-2]
+    num_pages = v.shape[1] if paged else 0
+    max_pages = block_table.shape[1] if paged else 0
+    desc = ReceiverDesc(dtype_code(v.dtype), lm.shape[0], sender_layers, lm.ctypes.data_as(_i32p),
+                        H_s, H_r, H_kv_r, d, B,
+                        v[0].numel() if v_layer_stride is None else v_layer_stride, o_layer_stride,
+                        _ptr(block_table), page_size, max_pages, num_pages, csr_capacity)
+    desc._keep = lm  # the layer map must outlive the descriptor
+    return desc
+
+
+def mapped_attn_v(desc: ReceiverDesc, batch: Batch, row_ptr, col_idx, values, W, v, o, stream=None):
+    _check(lib().mf_mapped_attn_v(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(row_ptr),
+                                  _ptr(col_idx), _ptr(values), _ptr(W), _ptr(v), _ptr(o),
+                                  _stream(stream)))

@@ -1,0 +1,90 @@
+"""The hot path as one call sequence over device tensors.
+
+sender side:   block statistics -> selection + extraction (staged compression)
+receiver side: fused mapped attention . V over the resident compressed state
+
+Only allocation and call order live here; all arithmetic is in libmapflow.so.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import torch
+
+from . import mapflow as mf
+
+
+@dataclasses.dataclass
+class SenderState:
+    """Compressed sender maps resident in HBM (one CSR over all layers)."""
+
+    desc: mf.SenderDesc
+    batch: mf.Batch
+    row_lse: torch.Tensor      # [L, H_s, Tq] fp32
+    block_mass: torch.Tensor   # [L, H_s, total_rb, max_cb] fp32
+    row_ptr: torch.Tensor      # [L*H_s*total_rb + 1] int32
+    col_idx: torch.Tensor      # [capacity] int32
+    values: torch.Tensor       # [capacity, B, B]
+    nnz: Optional[int]
+    workspace: torch.Tensor
+
+    @property
+    def B(self) -> int:
+        return self.desc.B
+
+
+def alloc_sender(batch: mf.Batch, q: torch.Tensor, k: torch.Tensor, B: int, capacity: int,
+                 sm_scale: float = 0.0) -> SenderState:
+    if q.dim() == 3:
+        q, k = q[None], k[None]
+    desc = mf.sender_desc(q, k, B, sm_scale)
+    L, H = desc.num_layers, desc.H_s
+    dev = q.device
+    row_lse = torch.empty((L, H, batch.info.total_q), dtype=torch.float32, device=dev)
+    block_mass = torch.empty((L, H, batch.total_rowblocks, max(batch.max_colblocks, 1)),
+                             dtype=torch.float32, device=dev)
+    row_ptr = torch.empty(L * H * batch.total_rowblocks + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+    values = torch.empty((max(capacity, 1), B, B), dtype=q.dtype, device=dev)
+    ws = torch.empty(max(mf.compress_workspace_size(desc, batch), 1), dtype=torch.uint8, device=dev)
+    return SenderState(desc, batch, row_lse, block_mass, row_ptr, col_idx, values, None, ws)
+
+
+def count_capacity(batch: mf.Batch, q, k, B: int, tau: float, sm_scale: float = 0.0) -> int:
+    """Kept-block count for (q, k, tau): stats + selection with no values (syncs once)."""
+    st = alloc_sender(batch, q, k, B, 0, sm_scale)
+    qq, kk = (q[None], k[None]) if q.dim() == 3 else (q, k)
+    mf.block_stats(st.desc, batch, qq, kk, st.row_lse, st.block_mass)
+    return mf.compress_blocks(st.desc, batch, qq, kk, st.row_lse, st.block_mass, tau, st.row_ptr,
+                              None, None, 0, st.workspace, sync_count=True)
+
+
+def compress(st: SenderState, q, k, tau: float, sync_count: bool = True, stream=None) -> SenderState:
+    qq, kk = (q[None], k[None]) if q.dim() == 3 else (q, k)
+    mf.block_stats(st.desc, st.batch, qq, kk, st.row_lse, st.block_mass, stream)
+    st.nnz = mf.compress_blocks(st.desc, st.batch, qq, kk, st.row_lse, st.block_mass, tau,
+                                st.row_ptr, st.col_idx, st.values, st.col_idx.numel(),
+                                st.workspace, sync_count, stream)
+    return st
+
+
+def mapped(st: SenderState, W: torch.Tensor, v: torch.Tensor, layer_map: Sequence[int],
+           out: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+           page_size: int = 0, stream=None) -> torch.Tensor:
+    """W [L_r, H_r, H_s] fp32; v [L_r, Tk, H_kv_r, d] (or a paged pool
+    [L_r, pages, page_size, H_kv_r, d] with block_table [S, max_pages]).
+    Returns O [L_r, Tq, H_r, d]."""
+    if W.dim() == 2:
+        W = W[None]
+    if v.dim() == (4 if block_table is not None else 3):
+        v = v[None]
+    L_r, H_r, H_s = W.shape
+    d = v.shape[-1]
+    Tq = st.batch.info.total_q
+    if out is None:
+        out = torch.empty((L_r, Tq, H_r, d), dtype=v.dtype, device=v.device)
+    desc = mf.receiver_desc(v, H_s, H_r, d, st.B, layer_map, st.desc.num_layers, out[0].numel(),
+                            st.col_idx.numel(), block_table, page_size)
+    mf.mapped_attn_v(desc, st.batch, st.row_ptr, st.col_idx, st.values, W, v, out, stream)
+    return out

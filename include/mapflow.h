@@ -1,0 +1,231 @@
+/*
+ * mapflow.h - C ABI of the MapFlow hot path on AMD Instinct MI355X (gfx950).
+ *
+ * MapFlow lets a receiver model reuse a sender model's attention map for the
+ * same context instead of recomputing its own (MapFlow page, 163.com,
+ * section "从内部表示,走向 token 之间的依赖关系").  This library runs the
+ * data-parallel part of that path on one GPU:
+ *
+ *   mf_block_stats      first stage of the staged compression: per query
+ *                       row-block, the attention probability mass of every
+ *                       causal B x B block, straight from the sender's Q and
+ *                       K, without forming the dense map (section
+ *                       "让复用真正省时…", paragraph "第一").
+ *   mf_compress_blocks  second stage: per (layer, sender head, row-block) keep
+ *                       the blocks needed to reach cumulative probability tau
+ *                       and extract their probabilities into a block-sparse
+ *                       CSR (same paragraph; kept counts differ per layer and
+ *                       position, paragraph "第二").
+ *   mf_mapped_attn_v    the fused step: read the kept blocks of every sender
+ *                       head, form the learned linear head combination on
+ *                       chip, multiply by the receiver's own V and accumulate
+ *                       the output, with no dense receiver map (paragraph
+ *                       "第三").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked DEVICE are GPU memory, HOST are CPU memory.  The caller
+ *     owns and allocates every buffer; the library allocates nothing.
+ *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = default
+ *     stream).  The only blocking call is mf_compress_blocks with a non-NULL
+ *     nnz_out, which synchronises `stream` once to read the kept-block count.
+ *   - Every argument is validated on the host before anything is launched;
+ *     a failing call returns a status other than MF_OK, launches nothing and
+ *     records a message for mf_last_error_message().  No exceptions or aborts
+ *     cross the ABI.
+ *   - Layouts are token-major: Q [T, H, d], K [T, H_kv, d], V [T, H_kv_r, d],
+ *     O [T, H_r, d], d contiguous.  Sequences of a batch are packed one after
+ *     another (varlen); a batch may hold prefill chunks, whose first query row
+ *     sits at position q_pos0 of its sequence while its keys cover the whole
+ *     prefix (chunked prefill, MapFlow page, paragraph "第三" and the closing
+ *     paragraph of that section on vLLM support for PagedAttention, chunked
+ *     prefill and varlen packing).
+ *   - Supported shapes: B in {32, 64, 128}; d in {64, 128}; 1 <= H <= 64 with
+ *     H_kv dividing H; dtype fp32 or bf16; chunk starts multiple of B; keys
+ *     of a sequence per call <= MF_MAX_KEYS.
+ *   - Thread safety: calls on distinct streams may run concurrently; the
+ *     compressed CSR is read-only for mf_mapped_attn_v, so any number of
+ *     receivers may read one sender state at once (paragraph "第二": one
+ *     sender state serves several downstream models).
+ */
+#ifndef MAPFLOW_H
+#define MAPFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MF_OK = 0,
+  MF_ERR_INVALID = 1,      /* null pointer, negative size, inconsistent layout */
+  MF_ERR_UNSUPPORTED = 2,  /* well-formed but outside the supported shapes */
+  MF_ERR_CAPACITY = 3,     /* more kept blocks than capacity_blocks (see below) */
+  MF_ERR_HIP = 4,          /* a HIP runtime call failed */
+  MF_ERR_WORKSPACE = 5     /* workspace missing or too small */
+} mf_status;
+
+typedef enum { MF_F32 = 0, MF_BF16 = 1 } mf_dtype;
+
+/* Longest key range of one sequence: the per-(row, column-block) statistics
+ * of one row-block live in on-chip LDS (about 4 bytes per key). */
+#define MF_MAX_KEYS 40448
+
+/* ------------------------------------------------------------------------ */
+/* Batch layout (varlen + chunked prefill)                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Sizes of a packed batch, filled by mf_plan. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t block;            /* B the plan was made for */
+  int32_t total_rowblocks;  /* sum over sequences of ceil(q_len / B) */
+  int32_t max_colblocks;    /* max over sequences of ceil(k_len / B) */
+  int32_t total_q;          /* packed query rows */
+  int32_t total_k;          /* packed keys (= value rows) */
+  int32_t max_k_len;
+  int32_t plan_len;         /* int32 words of the device plan: num_seqs + 1 + total_rowblocks */
+} mf_plan_info;
+
+/* Host-only.  Validates a packed batch and writes its row-block plan.
+ *   h_cu_seqlens_q  HOST [num_seqs+1]  query row offsets, non-decreasing, [0] = 0
+ *   h_cu_seqlens_k  HOST [num_seqs+1]  key offsets
+ *   h_q_pos0        HOST [num_seqs] or NULL  position of each chunk's first
+ *                   query row inside its sequence (multiple of B); NULL = 0
+ *   h_plan          HOST [plan_capacity] int32 or NULL: receives the plan, a
+ *                   prefix of row-block offsets per sequence (num_seqs + 1
+ *                   words) followed by the sequence of every row-block.  The
+ *                   caller copies it to the device and passes it in mf_batch.
+ * Requires k_len >= q_pos0 + q_len per sequence.  With h_plan NULL or
+ * plan_capacity < info->plan_len only `info` is filled and the call returns
+ * MF_ERR_CAPACITY, so a caller can size the buffer first. */
+mf_status mf_plan(const int32_t* h_cu_seqlens_q, const int32_t* h_cu_seqlens_k,
+                  const int32_t* h_q_pos0, int32_t num_seqs, int32_t B,
+                  int32_t* h_plan, int64_t plan_capacity, mf_plan_info* info);
+
+/* A packed batch as the kernels see it. */
+typedef struct {
+  mf_plan_info info;            /* from mf_plan */
+  const int32_t* cu_seqlens_q;  /* DEVICE [num_seqs+1] */
+  const int32_t* cu_seqlens_k;  /* DEVICE [num_seqs+1] */
+  const int32_t* q_pos0;        /* DEVICE [num_seqs] or NULL (all zero) */
+  const int32_t* plan;          /* DEVICE [info.plan_len] copy of mf_plan's h_plan */
+} mf_batch;
+
+/* ------------------------------------------------------------------------ */
+/* Sender side: staged block compression                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  mf_dtype dtype;           /* of Q, K and the packed block values */
+  int32_t num_layers;       /* sender layers compressed in one call */
+  int32_t H_s, H_kv_s;      /* query heads, key heads (H_kv_s divides H_s) */
+  int32_t d, B;             /* head dim, block size */
+  float sm_scale;           /* logit scale; 0 means 1/sqrt(d) */
+  int64_t layer_stride_q;   /* elements between layers of q (>= total_q*H_s*d) */
+  int64_t layer_stride_k;   /* elements between layers of k (>= total_k*H_kv_s*d) */
+} mf_sender_desc;
+
+/* Stage 1: block statistics.
+ *   q          DEVICE [num_layers][total_q][H_s][d]   (layer stride as above)
+ *   k          DEVICE [num_layers][total_k][H_kv_s][d]
+ *   row_lse    DEVICE fp32 [num_layers][H_s][total_q]: log sum_c exp(s_rc)
+ *              over the causal keys of each query row, s = sm_scale * q.k
+ *   block_mass DEVICE fp32 [num_layers][H_s][total_rowblocks][max_colblocks]:
+ *              m[i][j] = (sum of the softmax probabilities of block (i, j)) /
+ *              (valid rows of row-block i), so each row-block's masses sum to
+ *              1; entries past the row-block's causal range are 0.
+ * Row-block i of a sequence covers query positions [q_pos0 + iB, ...); its
+ * causal column blocks are 0 .. (position of its last row) / B. */
+mf_status mf_block_stats(const mf_sender_desc* desc, const mf_batch* batch,
+                         const void* q, const void* k,
+                         float* row_lse, float* block_mass, void* stream);
+
+/* Workspace bytes mf_compress_blocks needs for this batch. */
+size_t mf_compress_workspace_size(const mf_sender_desc* desc, const mf_batch* batch);
+
+/* Stage 2: selection and extraction.
+ * For every (layer l, sender head h, row-block i), sort its causal blocks by
+ * mass (descending; equal masses by ascending column block), and keep the
+ * shortest prefix whose cumulative mass (summed in fp64) reaches tau; tau = 1
+ * keeps every causal block.  The kept blocks form CSR row
+ * (l * H_s + h) * total_rowblocks + i:
+ *   row_ptr  DEVICE int32 [num_layers * H_s * total_rowblocks + 1]
+ *   col_idx  DEVICE int32 [capacity_blocks], ascending within a row
+ *   values   DEVICE [capacity_blocks][B][B] in dtype, or NULL (count only):
+ *            values[e][r][c] = exp(s_rc - row_lse_r) for query row r and key
+ *            column c of the block, exactly the sender's probabilities (not
+ *            renormalised), 0 where c is past row r or past the sequence.
+ * nnz_out HOST or NULL.  Non-NULL: the call synchronises `stream`, stores the
+ * number of kept blocks, and returns MF_ERR_CAPACITY (row_ptr valid,
+ * col_idx/values untouched) when it exceeds capacity_blocks; with col_idx
+ * NULL and capacity_blocks 0 it only counts (row_ptr and nnz) and succeeds.  NULL: nothing
+ * blocks; entries past capacity_blocks are dropped on the device, and
+ * row_ptr[last] always holds the true count, so a caller can check it later.
+ * tau must be in (0, 1].  workspace: DEVICE, at least
+ * mf_compress_workspace_size() bytes. */
+mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch,
+                             const void* q, const void* k,
+                             const float* row_lse, const float* block_mass, float tau,
+                             int32_t* row_ptr, int32_t* col_idx, void* values,
+                             int64_t capacity_blocks, int64_t* nnz_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Receiver side: fused mapped attention . V                                */
+/* ------------------------------------------------------------------------ */
+
+#define MF_MAX_LAYERS 256
+
+typedef struct {
+  mf_dtype dtype;             /* of the block values, V and O */
+  int32_t num_layers;         /* receiver mapped layers in this call */
+  int32_t sender_layers;      /* layers in the CSR (its num_layers) */
+  const int32_t* layer_map;   /* HOST [num_layers]: CSR layer each receiver layer
+                                 reads (layer mapping matches depths, section
+                                 "从内部表示…") */
+  int32_t H_s;                /* sender heads in the CSR */
+  int32_t H_r, H_kv_r;        /* receiver heads, value heads (H_kv_r divides H_r) */
+  int32_t d, B;
+  int64_t layer_stride_v;     /* elements between layers of v */
+  int64_t layer_stride_o;     /* elements between layers of o */
+  /* Paged values (PagedAttention).  block_table NULL: v is packed
+     [total_k][H_kv_r][d] per layer.  Otherwise v is a page pool
+     [num_pages][page_size][H_kv_r][d] per layer, and token t of sequence s
+     lives in page block_table[s * max_pages + t / page_size]. */
+  const int32_t* block_table; /* DEVICE [num_seqs][max_pages] or NULL */
+  int32_t page_size, max_pages;
+  int64_t num_pages;          /* pages per layer of the pool; page ids are clamped to it */
+  int64_t csr_capacity;       /* entries of col_idx / values; CSR entries past it are ignored */
+} mf_receiver_desc;
+
+/* O_r[i] = sum over blocks j kept by any sender head of
+ *          (sum_{h keeps j} W[r][h] * P_h[i][j]) . V_{g(r)}[j]
+ * for every receiver layer, row-block i and receiver head r, where P_h are the
+ * packed values of CSR layer layer_map[l] and g(r) = r / (H_r / H_kv_r).
+ *   row_ptr, col_idx, values  DEVICE, as written by mf_compress_blocks
+ *   W    DEVICE fp32 [num_layers][H_r][H_s]  learned head mapping
+ *   v    DEVICE values (packed or paged, see above)
+ *   o    DEVICE [num_layers][total_q][H_r][d] in dtype; overwritten
+ * The CSR must come from a compression of the same batch layout. */
+mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const void* values, const float* W, const void* v,
+                           void* o, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                              */
+/* ------------------------------------------------------------------------ */
+
+const char* mf_status_string(mf_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* mf_last_error_message(void);
+/* Library version, e.g. "mapflow-mi355x 0.1". */
+const char* mf_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAPFLOW_H */

@@ -1,0 +1,194 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+plans batches, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from cross_model_attention_mf_amd import mapflow as mf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mapflow.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mf_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert set(decl) == set(mf.EXPORTS), decl
+
+
+def test_library_exports_every_declared_symbol():
+    L = mf.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.mf_version().decode().startswith("mapflow-mi355x")
+    assert L.mf_status_string(3).decode() == "MF_ERR_CAPACITY"
+
+
+def _c_layout(tmp_path):
+    """Offsets and sizes of the header's structs as gcc lays them out."""
+    import subprocess
+    fields = {
+        "mf_plan_info": [f for f, _ in mf.PlanInfo._fields_],
+        "mf_batch": [f for f, _ in mf.BatchC._fields_],
+        "mf_sender_desc": [f for f, _ in mf.SenderDesc._fields_],
+        "mf_receiver_desc": [f for f, _ in mf.ReceiverDesc._fields_],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mapflow.h"', 'int main(void) {']
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} sizeof %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    return {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out.splitlines()}
+
+
+def test_struct_layouts_match_header(tmp_path):
+    c = _c_layout(tmp_path)
+    for name, cls in [("mf_plan_info", mf.PlanInfo), ("mf_batch", mf.BatchC),
+                      ("mf_sender_desc", mf.SenderDesc), ("mf_receiver_desc", mf.ReceiverDesc)]:
+        assert c[(name, "sizeof")] == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert c[(name, f)] == getattr(cls, f).offset, (name, f)
+
+
+def test_plan_layout():
+    cu_q = [0, 100, 164, 164, 400]
+    cu_k = [0, 228, 292, 300, 936]
+    p0 = [128, 0, 0, 384]
+    info, plan = mf.plan(cu_q, cu_k, p0, 64)
+    assert info.total_rowblocks == 2 + 1 + 0 + 4
+    assert info.max_colblocks == (636 + 63) // 64
+    assert info.total_q == 400 and info.total_k == 936 and info.max_k_len == 636
+    assert list(plan[:5]) == [0, 2, 3, 3, 7]
+    assert list(plan[5:]) == [0, 0, 1, 3, 3, 3, 3]
+
+
+@pytest.mark.parametrize("args,status", [
+    (([0, 10], [0, 5], None, 64), mf.MF_ERR_INVALID),          # keys do not cover queries
+    (([0, 10], [0, 40], [30], 64), mf.MF_ERR_UNSUPPORTED),     # chunk not on a block edge
+    (([0, 10], [0, 10], None, 48), mf.MF_ERR_UNSUPPORTED),     # unsupported B
+    (([0, 10, 5], [0, 10, 20], None, 64), mf.MF_ERR_INVALID),  # negative length
+    (([1, 10], [0, 10], None, 64), mf.MF_ERR_INVALID),         # offsets must start at 0
+    (([0, 10], [0, 50000], None, 64), mf.MF_ERR_UNSUPPORTED),  # longer than MF_MAX_KEYS
+])
+def test_plan_errors(args, status):
+    with pytest.raises(mf.MapflowError) as e:
+        mf.plan(*args)
+    assert e.value.status == status
+
+
+def _host_batch(cu_q, cu_k, q_pos0, B):
+    """A batch whose device pointers are fake: only for calls that must fail
+    validation (or do nothing) before touching the GPU."""
+    info, _ = mf.plan(cu_q, cu_k, q_pos0, B)
+    b = mf.BatchC(info, 16, 16, None, 16)
+    return b
+
+
+def _sender(**kw):
+    base = dict(dtype=mf.MF_BF16, num_layers=1, H_s=4, H_kv_s=4, d=128, B=64, sm_scale=0.0,
+                layer_stride_q=0, layer_stride_k=0)
+    base.update(kw)
+    return mf.SenderDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=48), mf.MF_ERR_UNSUPPORTED),
+    (dict(d=96), mf.MF_ERR_UNSUPPORTED),
+    (dict(H_s=65, H_kv_s=65), mf.MF_ERR_UNSUPPORTED),
+    (dict(H_kv_s=3), mf.MF_ERR_INVALID),
+    (dict(dtype=7), mf.MF_ERR_INVALID),
+    (dict(num_layers=-1), mf.MF_ERR_INVALID),
+    (dict(sm_scale=float("nan")), mf.MF_ERR_INVALID),
+    (dict(num_layers=2, layer_stride_q=5, layer_stride_k=5), mf.MF_ERR_INVALID),
+])
+def test_block_stats_validation(kw, status):
+    b = _host_batch([0, 256], [0, 256], None, kw.get("B", 64) if kw.get("B", 64) in (32, 64, 128) else 64)
+    d = _sender(**kw)
+    st = mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None)
+    assert st == status, mf.lib().mf_last_error_message()
+    assert mf.lib().mf_last_error_message().decode()
+
+
+def test_block_mismatch_between_plan_and_desc():
+    b = _host_batch([0, 256], [0, 256], None, 32)
+    d = _sender(B=64)
+    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None) == mf.MF_ERR_INVALID
+
+
+def test_empty_batch_is_a_noop():
+    b = _host_batch([0], [0], None, 64)
+    d = _sender()
+    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), None, None, None, None, None) == mf.MF_OK
+
+
+@pytest.mark.parametrize("tau", [0.0, -0.5, 1.5, float("nan")])
+def test_compress_rejects_tau(tau):
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    d = _sender()
+    nnz = ctypes.c_int64(0)
+    st = mf.lib().mf_compress_blocks(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, tau, 16, 16, 16,
+                                     10, ctypes.byref(nnz), 16, 1 << 20, None)
+    assert st == mf.MF_ERR_INVALID
+
+
+def test_compress_workspace_checks():
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    d = _sender()
+    need = mf.lib().mf_compress_workspace_size(ctypes.byref(d), ctypes.byref(b))
+    rows = 1 * 4 * 4
+    assert need >= rows * 4 + rows * 1 * 4
+    st = mf.lib().mf_compress_blocks(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, 0.9, 16, 16, 16,
+                                     10, None, 16, need - 1, None)
+    assert st == mf.MF_ERR_WORKSPACE
+    st = mf.lib().mf_compress_blocks(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, 0.9, 16, 16, 16,
+                                     -1, None, 16, need, None)
+    assert st == mf.MF_ERR_INVALID
+
+
+def _receiver(layer_map, **kw):
+    lm = np.asarray(layer_map, dtype=np.int32)
+    base = dict(dtype=mf.MF_BF16, num_layers=len(layer_map), sender_layers=2,
+                layer_map=lm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), H_s=4, H_r=3, H_kv_r=3,
+                d=128, B=64, layer_stride_v=1 << 30, layer_stride_o=1 << 30, block_table=None,
+                page_size=0, max_pages=0, num_pages=0, csr_capacity=16)
+    base.update(kw)
+    r = mf.ReceiverDesc(**base)
+    r._keep = lm
+    return r
+
+
+@pytest.mark.parametrize("layer_map,kw,status", [
+    ([0, 2], {}, mf.MF_ERR_INVALID),                       # sender layer out of range
+    ([0, -1], {}, mf.MF_ERR_INVALID),
+    ([0], dict(H_kv_r=2), mf.MF_ERR_INVALID),               # kv heads do not divide
+    ([0], dict(H_s=0), mf.MF_ERR_UNSUPPORTED),
+    ([0], dict(block_table=16, page_size=0, max_pages=4, num_pages=4), mf.MF_ERR_INVALID),
+    ([0], dict(block_table=16, page_size=16, max_pages=1, num_pages=4), mf.MF_ERR_INVALID),  # table too short
+])
+def test_mapped_validation(layer_map, kw, status):
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    r = _receiver(layer_map, **kw)
+    st = mf.lib().mf_mapped_attn_v(ctypes.byref(r), ctypes.byref(b), 16, 16, 16, 16, 16, 16, None)
+    assert st == status, mf.lib().mf_last_error_message()
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mf, "_lib", None)
+    monkeypatch.setattr(mf, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        mf.lib()
