@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rowblocks", type=int, default=6)
+    ap.add_argument("--cpu-sample-rowblocks", type=int, default=48)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()

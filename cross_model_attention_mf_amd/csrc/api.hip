@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "errors.h"
@@ -244,7 +245,9 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, 
   a.L = desc->num_layers; a.Ls = desc->sender_layers; a.Hs = desc->H_s; a.Hr = desc->H_r; a.Hkv = desc->H_kv_r;
   a.d = desc->d; a.B = desc->B;
   for (int l = 0; l < desc->num_layers; ++l) a.layer_map[l] = desc->layer_map[l];
-  const int e = mf::launch_mapped(a, desc->dtype, stream);
+  const char* pv = getenv("MF_PORTABLE_MAPPED");
+  const bool allow_fast = !(pv && pv[0] == '1');
+  const int e = mf::launch_mapped(a, desc->dtype, stream, allow_fast, device_lds_limit());
   return e ? hip_fail(e, fn) : MF_OK;
 }
 

@@ -82,6 +82,32 @@ __device__ __forceinline__ RowBlockInfo rowblock_info(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// XCD-aware work order.  Workgroups are dealt round-robin to the 8 XCDs
+// (linear id n runs on XCD n % 8), and each XCD has its own L2.  Work items
+// (rb fastest, then h, then l) are cut into 8 contiguous ranges, one per XCD,
+// so the row-blocks of one (layer, head) run together on one XCD and share
+// its L2 for K.  Linear ids past the end of the work return l = L (exit).
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+__host__ __device__ inline unsigned xcd_grid(int nrb, int H, int L) {
+  const long long n = (long long)nrb * H * L;
+  const long long per = (n + kXcds - 1) / kXcds;
+  return (unsigned)(per * kXcds);
+}
+
+__device__ __forceinline__ void xcd_unflatten(unsigned bid, int nrb, int H, int L, int& rb, int& h, int& l) {
+  const long long n = (long long)nrb * H * L;
+  const long long per = (n + kXcds - 1) / kXcds;
+  const long long item = (long long)(bid % kXcds) * per + bid / kXcds;
+  if (item >= n) { rb = 0; h = 0; l = L; return; }
+  rb = (int)(item % nrb);
+  const long long t = item / nrb;
+  h = (int)(t % H);
+  l = (int)(t / H);
+}
+
+// ---------------------------------------------------------------------------
 // MFMA score tile: S[16 rows x 16 cols] = Q_rows . K_cols^T over D.
 // Lane L of a wave supplies row/col L%16 and the k-slice selected by L/16;
 // the output holds S[4*(L/16)+i][L%16] in element i (checked on gfx950).

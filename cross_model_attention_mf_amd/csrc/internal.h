@@ -88,7 +88,7 @@ size_t block_stats_lds_bytes(int B, int max_cb);
 int launch_select(const SelectArgs& a, void* stream);
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream);
-int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream);
+int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);
 size_t select_lds_bytes(int max_cb);
 
 }  // namespace mf

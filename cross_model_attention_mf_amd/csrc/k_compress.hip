@@ -10,8 +10,8 @@
 //   scan:    one workgroup turns the counts into row_ptr (exclusive scan).
 //   extract: one workgroup per CSR row recomputes S = Q K^T for its kept
 //            blocks only (MFMA), P = exp(S * scale - row_lse), and writes
-//            B x B values row-major through an LDS transpose so every store
-//            is a full 16-byte vector.
+//            each B x B block key-major (values[e][key][query]) through LDS
+//            so every store is a full 16-byte vector.
 #include "device_common.h"
 #include "internal.h"
 
@@ -127,9 +127,12 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
   constexpr int NT = B / 16;
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte store
   constexpr int PITCH = B + VEC;               // LDS row pitch (elements)
-  __shared__ __align__(16) T tile[B / 16][16 * PITCH];
+  // the block, key-major: tile[c][q]
+  __shared__ __align__(16) T tile[B * PITCH];
 
-  const int rb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  int rb, h, l;
+  xcd_unflatten(blockIdx.x, a.b.total_rb, a.H, a.L, rb, h, l);
+  if (l >= a.L) return;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
   const size_t lh = (size_t)l * a.H + h;
   const size_t row = lh * a.b.total_rb + rb;
@@ -160,7 +163,6 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
   }
   const uint32_t* __restrict__ kb = a.keep_bits + row * (size_t)a.words;
   T* __restrict__ vals = reinterpret_cast<T*>(a.values);
-  T* __restrict__ my = tile[w];
 
   int64_t e = base;
   for (int wd = 0; wd < a.words; ++wd) {
@@ -179,26 +181,27 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
             acc[nt] = qf.dot(kbase + (size_t)c * kstride, lane, acc[nt]);
           }
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt) {
+            const int c = j * B + 16 * nt + lr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int c = j * B + 16 * nt + lr;
               float p = 0.f;
               if (rowl[i] < ri.rows && c <= ri.pos0 + rowl[i]) {
                 float x = fmaf(acc[nt][i], s_hi, -lse[i]);
                 x = fmaf(acc[nt][i], s_lo, x);
                 p = exp2f(x * kLog2e);
               }
-              my[(4 * lg + i) * PITCH + 16 * nt + lr] = from_f32<T>(p);
+              tile[(16 * nt + lr) * PITCH + rowl[i]] = from_f32<T>(p);
             }
+          }
           __syncthreads();
-          // 16 rows x B columns of this wave -> global, 16 bytes per lane store
-          T* __restrict__ dst = vals + (size_t)e * B * B + (size_t)(16 * w) * B;
-          constexpr int CH = 16 * B / VEC;
-          for (int c = lane; c < CH; c += 64) {
+          // B key rows of B queries each -> global, 16 bytes per store
+          T* __restrict__ dst = vals + (size_t)e * B * B;
+          constexpr int CH = B * B / VEC;
+          for (int c = threadIdx.x; c < CH; c += B * 4) {
             const int r = c / (B / VEC), col = (c % (B / VEC)) * VEC;
             *reinterpret_cast<uint4*>(dst + (size_t)r * B + col) =
-                *reinterpret_cast<const uint4*>(my + r * PITCH + col);
+                *reinterpret_cast<const uint4*>(tile + r * PITCH + col);
           }
           __syncthreads();
         }
@@ -210,7 +213,7 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
 
 template <typename T, int B, int D>
 int launch_ex(const ExtractArgs& a, void* stream) {
-  dim3 grid(a.b.total_rb, a.H, a.L);
+  dim3 grid(xcd_grid(a.b.total_rb, a.H, a.L));
   hipLaunchKernelGGL((extract_kernel<T, B, D>), grid, dim3(B * 4), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }

@@ -63,6 +63,7 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
     const int j = j_s;
     if (j == 0x7FFFFFFF) break;
     const unsigned long long mask = mask_s;
+    // values are key-major: element (query q, key c) of a block sits at c*B + q
     for (int pos = tid; pos < B * B; pos += kMapThreads) {
       float acc = 0.f;
       unsigned long long mm = mask;
@@ -71,7 +72,7 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
         mm &= mm - 1;
         acc += Wr[h] * to_f32(vals[(size_t)vptr[h] * B * B + pos]);
       }
-      A[pos] = acc;
+      A[(pos % B) * B + pos / B] = acc;
     }
     __syncthreads();
     for (int c = 0; c < B; ++c) {
@@ -100,6 +101,386 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernel (bf16).  One workgroup per (receiver layer, row-block, 64-row
+// half of a 128-row block, group of 8 receiver heads); 2 x RQ/16 waves, wave
+// (hq, qt) owning receiver heads 4hq..4hq+3 of the group and query rows
+// 16qt..16qt+15.  Each block j of the union of the sender heads' kept sets is
+// walked in 32-key steps; a step is 4 stages g2 = 0..3, and stage g2 stages
+// the 8 keys 32cb + 8 g2 + e (e = 0..7) of every sender head in LDS.
+//
+//   head mix (MFMA 16x16x32, K = sender heads, W block-diagonal in the key
+//   group):  C_e[(g, r)][q] += sum_h [g == g2] W[r][h] P_h[32cb + 8 g2 + e][q]
+//   so after the 4 stages lane (g, q) holds, for e = 0..7, the mixed map
+//   A_r[q][32cb + 8g + e]: exactly the A operand (8 keys per lane group) of
+//   the P.V MFMA, and the mixed map never leaves registers;
+//   P.V (MFMA 16x16x32, K = keys): O_r[q][n] += A_r[q][c] V_r[c][n].
+//
+// Memory pipeline: key-major block rows (RQ contiguous queries) and V rows
+// are copied HBM -> LDS with global_load_lds (16 bytes per lane, no
+// registers); stages are double-buffered, the next stage's copies are issued
+// right after the barrier that opens the current one, and the V rows of a
+// 32-key step are issued at its first stage and used after its last.  The
+// column lists of the sender heads and the page ids of paged values also
+// arrive through async LDS copies, so no register-dependent load drains the
+// pipeline.  Every lane of every copy instruction loads (absent heads and
+// keys past the sequence read a valid row whose finite values meet zero
+// weights or zero probabilities).  Operands are read with ds_read_tr16_b64
+// (lane t of a 16-lane group gets column t of a 4-row tile) from rows whose
+// 16-byte chunks are XOR-swizzled.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ bf16x4 tr_read(const char* lds_generic, unsigned byte_off) {
+  auto p = (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)
+           ((uintptr_t)lds_generic) + byte_off);
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ void async_copy16(const void* gsrc, char* lds_generic_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)((uintptr_t)lds_generic_base), 16, 0, 0);
+}
+__device__ __forceinline__ void async_copy4(const void* gsrc, char* lds_generic_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)((uintptr_t)lds_generic_base), 4, 0, 0);
+}
+
+// A copy of a lane value the compiler cannot see through: per-stage address
+// math derived from it is recomputed in place (a few VALU ops) instead of
+// being hoisted out of the stage loop and pinned in registers.
+__device__ __forceinline__ int opaque(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
+// chunk swizzle of LDS rows (16-byte chunks): spreads the rows a transpose
+// read touches together over distinct bank groups
+__device__ __forceinline__ int swz(int row, int cpr) { return ((row & 3) | ((row >> 1) & 0xC)) & (cpr - 1); }
+
+struct alignas(16) UnionInfo {
+  int j;
+  int pad;
+  unsigned long long mask;
+  int vidx[64];
+  int page[128];
+};
+
+template <int B, int D, int HP8>
+struct MapCfg {
+  static constexpr int RQ = B < 64 ? B : 64;          // query rows per workgroup
+  static constexpr int NQT = RQ / 16;                  // query tiles
+  static constexpr int NW = 2 * NQT;                   // waves
+  static constexpr int NT = D / 16;                    // 16-wide n tiles of d
+  static constexpr int CB = B / 32;                    // 32-key steps per block
+  static constexpr int QH = B / RQ;                    // workgroups per row-block
+  static constexpr int PROW = RQ * 2;                  // bytes per P row (one key, RQ queries)
+  static constexpr int PCPR = PROW / 16;               // 16-byte chunks per P row
+  static constexpr int VROW = D * 2;                   // bytes per V row
+  static constexpr int VCPR = VROW / 16;
+  static constexpr int VBYTES = 8 * 32 * VROW;         // 8 heads x 32 keys
+  static constexpr int HPAD = 8 * HP8;
+  static constexpr int SBYTES = 8 * HPAD * PROW;       // one stage: 8 keys x all heads
+  static constexpr int PI = SBYTES / 1024;             // copy instructions per stage
+  static constexpr int VI = VBYTES / 1024;             // copy instructions per step for V
+};
+
+size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
+  const int hpad = (Hs + 7) / 8 * 8;
+  const int RQ = B < 64 ? B : 64;
+  const size_t stage = (size_t)8 * hpad * RQ * 2;
+  const size_t vbytes = (size_t)8 * 32 * D * 2;
+  const size_t obytes = (size_t)RQ * 8 * D * 2;       // output staging (aliases the stages and V)
+  size_t main = 2 * stage + vbytes;
+  if (obytes > main) main = obytes;
+  return main + 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
+}
+
+template <int B, int D, int HP8>
+__global__ void __launch_bounds__(((B < 64 ? B : 64) / 16) * 2 * 64)
+mapped_mfma_kernel(MappedArgs a, int ngroups) {
+  using C = MapCfg<B, D, HP8>;
+  constexpr int hpad = C::HPAD;
+  extern __shared__ __align__(16) char smem[];
+  char* stages = smem;
+  char* Vs = smem + 2 * C::SBYTES;
+  size_t main_bytes = 2 * C::SBYTES + C::VBYTES;
+  if ((size_t)C::RQ * 8 * D * 2 > main_bytes) main_bytes = (size_t)C::RQ * 8 * D * 2;
+  UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + main_bytes);
+  int* curcol = reinterpret_cast<int*>(UI + 2);        // next column of each sender head
+  float* Wsh = reinterpret_cast<float*>(curcol + 64);   // [8 receiver heads][64 sender heads]
+
+  // ---- work item (XCD-aware: the head groups of one row-block share an XCD)
+  const int nitems = a.b.total_rb * C::QH;
+  int item, grp, l;
+  {
+    const long long n = (long long)nitems * ngroups * a.L;
+    const long long per = (n + kXcds - 1) / kXcds;
+    const long long w = (long long)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (w >= n) return;
+    grp = (int)(w % ngroups);
+    const long long t = w / ngroups;
+    item = (int)(t % nitems);
+    l = (int)(t / nitems);
+  }
+  const int rb = item / C::QH, qoff = (item % C::QH) * C::RQ;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
+  const int sl = a.layer_map[l];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hq = wave / C::NQT, qt = wave % C::NQT;
+  const int lg = lane >> 4, lr = lane & 15;
+  const bool paged = a.block_table != nullptr;
+
+  // ---- zero the stages and V rows, load the group's W rows
+  for (size_t o = (size_t)tid * 16; o < main_bytes; o += (size_t)C::NW * 64 * 16)
+    *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
+  for (int t = tid; t < 8 * 64; t += C::NW * 64) {
+    const int rl = t >> 6, h = t & 63, r = 8 * grp + rl;
+    Wsh[t] = (h < a.Hs && r < a.Hr) ? a.W[((size_t)l * a.Hr + r) * a.Hs + h] : 0.f;
+  }
+
+  // ---- union merge state (wave 0): lane h walks sender head h's sorted list
+  int64_t mptr = 0, mend = 0;
+  if (wave == 0) {
+    int c0 = 0x7FFFFFFF;
+    if (lane < a.Hs) {
+      const size_t row = ((size_t)sl * a.Hs + lane) * a.b.total_rb + rb;
+      mptr = min((int64_t)a.row_ptr[row], a.csr_capacity);
+      mend = min((int64_t)a.row_ptr[row + 1], a.csr_capacity);
+      if (mptr < mend) c0 = a.col_idx[mptr];
+    }
+    curcol[lane] = c0;
+  }
+  // wave 0: next block of the union and the heads that keep it; the heads'
+  // next columns and the block's page ids arrive asynchronously in LDS
+  auto merge = [&](UnionInfo* out) {
+    const int mcur = curcol[lane];
+    int jm = mcur;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) jm = min(jm, __shfl_xor(jm, off, 64));
+    const bool take = (mcur == jm) && (mcur != 0x7FFFFFFF);
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      out->vidx[lane] = (int)mptr;
+      ++mptr;
+      if (mptr < mend) async_copy4(a.col_idx + mptr, reinterpret_cast<char*>(curcol));
+      else curcol[lane] = 0x7FFFFFFF;
+    }
+    if (lane == 0) { out->j = jm; out->mask = m; }
+    if (paged && jm != 0x7FFFFFFF) {
+      for (int k0 = 0; k0 < B; k0 += 64) {
+        const int key = min(jm * B + k0 + lane, ri.klen - 1);
+        async_copy4(a.block_table + (size_t)ri.seq * a.max_pages + key / a.page_size,
+                    reinterpret_cast<char*>(out->page + k0));
+      }
+    }
+  };
+  __syncthreads();
+  if (wave == 0) merge(&UI[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
+  const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)l * a.lsv;
+
+  // stage (union info, step cb, key group g2): keys 32cb + 8 g2 + e of all
+  // heads -> stage buffer; row 8h + e holds RQ queries of head h, key e
+  auto issue_p = [&](const UnionInfo* ui, int cb, int g2, char* buf) {
+    constexpr int RPI = 1024 / C::PROW;                // rows per copy instruction
+    const unsigned long long mk = ui->mask;
+    const int ln = opaque(lane);
+    for (int k = wave; k < C::PI; k += C::NW) {
+      const int rho = k * RPI + ln / C::PCPR;
+      const int p = ln % C::PCPR;
+      const int h = rho >> 3, e = rho & 7;
+      const int lc = p ^ swz(rho, C::PCPR);
+      const bool live = h < a.Hs && ((mk >> h) & 1ull);
+      const bf16* src = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)(32 * cb + 8 * g2 + e) * B + qoff + 8 * lc
+                             : vals + 8 * lc;
+      async_copy16(src, buf + (size_t)k * 1024);
+    }
+  };
+  // V rows of a 32-key step for the group's 8 receiver heads -> Vs
+  auto issue_v = [&](const UnionInfo* ui, int cb) {
+    constexpr int RPI = 1024 / C::VROW;
+    const int ln = opaque(lane);
+    for (int k = wave; k < C::VI; k += C::NW) {
+      const int rho = k * RPI + ln / C::VCPR;          // row = r_local * 32 + c_local
+      const int p = ln % C::VCPR;
+      const int rl = rho / 32, cl = rho % 32;
+      const int r = 8 * grp + rl;
+      const int kl = 32 * cb + cl;                     // key inside the block
+      const int key = ui->j * B + kl;
+      const bool live = r < a.Hr && key < ri.klen;
+      const int g = live ? r / (a.Hr / a.Hkv) : 0;
+      const int lc = p ^ swz(rho, C::VCPR);
+      size_t tok;
+      if (paged) {
+        int64_t page = live ? ui->page[kl] : 0;
+        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+        tok = live ? (size_t)page * a.page_size + key % a.page_size : 0;
+      } else {
+        tok = (size_t)ri.k0 + (live ? key : 0);
+      }
+      async_copy16(vbase + (tok * a.Hkv + g) * D + 8 * lc, Vs + (size_t)k * 1024);
+    }
+  };
+
+  f32x4 O[4][C::NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) O[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // per-lane transpose-read offsets inside a stage buffer: rows 8h + e of the
+  // lane's 4-head group (two reads: heads 8lg + (lr>>2) and + 4), columns q
+  const int q = 16 * qt + 4 * (lr & 3);
+  const int plc = q >> 3, pwithin = (q & 7) * 2;
+  const float* wrow = Wsh + (4 * hq + (lr & 3)) * 64;
+
+  if (UI[0].j != 0x7FFFFFFF) {
+    issue_p(&UI[0], 0, 0, stages);
+    int u = 0, cb = 0, g2 = 0, s = 0;
+    bf16x8 Wk[2];
+    f32x4 Cacc[8];
+    for (;;) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const UnionInfo* ui = &UI[u & 1];
+      if (g2 == 0) {
+        if (cb == 0) {
+          if (wave == 0) merge(&UI[(u + 1) & 1]);
+          // W of this union block: sender heads that do not keep j get weight 0
+          const unsigned long long mk = ui->mask;
+#pragma unroll
+          for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) {
+              const int h = 32 * hk + 8 * lg + ee;
+              Wk[hk][ee] = (bf16)(((mk >> h) & 1ull) ? wrow[h] : 0.f);
+            }
+        }
+        issue_v(ui, cb);
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // ---- issue the next stage (if any) into the other buffer
+      int nu = u, ncb = cb, ng2 = g2 + 1;
+      if (ng2 == 4) { ng2 = 0; if (++ncb == C::CB) { ncb = 0; ++nu; } }
+      const bool more = (nu == u) || UI[nu & 1].j != 0x7FFFFFFF;
+      if (more) issue_p(&UI[nu & 1], ncb, ng2, stages + (size_t)((s + 1) & 1) * C::SBYTES);
+
+      // ---- head mix over the 8 keys of key group g2: lanes of key group g2
+      // take W, the others zero (block-diagonal)
+      const char* cur = stages + (size_t)(s & 1) * C::SBYTES;
+      const bf16x8 zero8 = {};
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        if (32 * hk < hpad) {
+          const bf16x8 wop = ((lr >> 2) == g2) ? Wk[hk] : zero8;
+          const int hbase = 32 * hk + 8 * lg;
+          const bool hv = hbase < hpad;
+          const int rho0 = 8 * (hbase + (lr >> 2));     // row of key e = 0, first head of the read
+          const int sw = swz(rho0, C::PCPR);            // same for rows rho0 + e and rho0 + 32
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            bf16x8 pop = zero8;
+            if (hv) {
+              const unsigned off = (unsigned)((rho0 + e) * C::PROW + ((plc ^ (sw ^ swz(e, C::PCPR))) << 4) + pwithin);
+              const bf16x4 lo = tr_read(cur, off);
+              const bf16x4 hi = tr_read(cur, off + 32 * C::PROW);
+              pop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop, Cacc[e], 0, 0, 0);
+          }
+        }
+      }
+      if (g2 == 3) {
+        // ---- P.V for this 32-key step: A_r[q][32cb + 8lg + e] = Cacc[e][i]
+        bf16x8 Aop[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int ee = 0; ee < 8; ++ee) Aop[i][ee] = (bf16)Cacc[ee][i];
+        const int nlo = 4 * (lr & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rho0 = (4 * hq + i) * 32 + 8 * lg + (lr >> 2);
+          const int sw0 = swz(rho0, C::VCPR);           // same for rho0 + 4
+#pragma unroll
+          for (int nt = 0; nt < C::NT; ++nt) {
+            const int n = 16 * nt + nlo;
+            const int lc = n >> 3, within = (n & 7) * 2;
+            const unsigned off = (unsigned)(rho0 * C::VROW + ((lc ^ sw0) << 4) + within);
+            const bf16x4 lo = tr_read(Vs, off);
+            const bf16x4 hi = tr_read(Vs, off + 4 * C::VROW);
+            const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            O[i][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[i], vop, O[i][nt], 0, 0, 0);
+          }
+        }
+      }
+      if (!more) break;
+      u = nu; cb = ncb; g2 = ng2; ++s;
+    }
+  }
+
+  // ---- output: stage [q][8 heads][d] in LDS, then 16-byte stores of whole rows
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  bf16* stage = reinterpret_cast<bf16*>(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int qq = 16 * qt + 4 * lg + ii;
+        stage[((size_t)qq * 8 + 4 * hq + i) * D + 16 * nt + lr] = (bf16)O[i][nt][ii];
+      }
+  __syncthreads();
+  bf16* __restrict__ obase = reinterpret_cast<bf16*>(a.o) + (size_t)l * a.lso;
+  const int heads_here = min(8, a.Hr - 8 * grp);
+  constexpr int CPQ = 8 * D * 2 / 16;                  // 16-byte chunks per query row
+  for (int c = tid; c < C::RQ * CPQ; c += C::NW * 64) {
+    const int qq = c / CPQ, k = c % CPQ;
+    const int hl = (k * 8) / D;
+    if (qoff + qq < ri.rows && hl < heads_here) {
+      bf16* dst = obase + ((size_t)(ri.q0 + qoff + qq) * a.Hr + 8 * grp) * D + (size_t)k * 8;
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stage + (size_t)qq * 8 * D + (size_t)k * 8);
+    }
+  }
+}
+
+template <int B, int D, int HP8>
+int launch_fast_h(const MappedArgs& a, void* stream) {
+  using C = MapCfg<B, D, HP8>;
+  const size_t lds = mapped_mfma_lds_bytes(B, D, a.Hs);
+  auto kern = mapped_mfma_kernel<B, D, HP8>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return (int)e;
+  const int ngroups = (a.Hr + 7) / 8;
+  const long long n = (long long)a.b.total_rb * C::QH * ngroups * a.L;
+  const long long per = (n + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per * kXcds)), dim3(C::NW * 64), lds, (hipStream_t)stream, a, ngroups);
+  return (int)hipGetLastError();
+}
+
+template <int B, int D>
+int launch_fast(const MappedArgs& a, void* stream) {
+  switch ((a.Hs + 7) / 8) {
+    case 1: return launch_fast_h<B, D, 1>(a, stream);
+    case 2: return launch_fast_h<B, D, 2>(a, stream);
+    case 3: return launch_fast_h<B, D, 3>(a, stream);
+    case 4: return launch_fast_h<B, D, 4>(a, stream);
+    case 5: return launch_fast_h<B, D, 5>(a, stream);
+    case 6: return launch_fast_h<B, D, 6>(a, stream);
+    case 7: return launch_fast_h<B, D, 7>(a, stream);
+    case 8: return launch_fast_h<B, D, 8>(a, stream);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
 template <typename T, int B, int D>
 int launch_g(const MappedArgs& a, void* stream) {
   dim3 grid(a.b.total_rb, a.Hr, a.L);
@@ -122,8 +503,18 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 }  // namespace
 
-int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream) {
+int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
+  if (dt == MF_BF16 && allow_fast && mapped_mfma_lds_bytes(a.B, a.d, a.Hs) <= lds_limit) {
+    switch (a.B * 1000 + a.d) {
+      case 32064: return launch_fast<32, 64>(a, stream);
+      case 32128: return launch_fast<32, 128>(a, stream);
+      case 64064: return launch_fast<64, 64>(a, stream);
+      case 64128: return launch_fast<64, 128>(a, stream);
+      case 128064: return launch_fast<128, 64>(a, stream);
+      case 128128: return launch_fast<128, 128>(a, stream);
+    }
+  }
   return dt == MF_BF16 ? launch_gd<bf16>(a, stream) : launch_gd<float>(a, stream);
 }
 

@@ -32,10 +32,11 @@ block_stats_kernel(StatsArgs a) {
   float* E = reinterpret_cast<float*>(smem);
   double* LSE = reinterpret_cast<double*>(smem + ((size_t)B * ecols * 4 + 15) / 16 * 16);
 
+  int rbi, h, l;
+  xcd_unflatten(blockIdx.x, a.b.total_rb, a.H, a.L, rbi, h, l);
+  if (l >= a.L) return;
   // heaviest (latest) row-blocks first: causal work grows with position
-  const int rb = a.b.total_rb - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int l = blockIdx.z;
+  const int rb = a.b.total_rb - 1 - rbi;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
   const int hk = h / (a.H / a.Hkv);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -146,7 +147,7 @@ int launch_t(const StatsArgs& a, void* stream) {
   auto kern = block_stats_kernel<T, B, D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;
-  dim3 grid(a.b.total_rb, a.H, a.L);
+  dim3 grid(xcd_grid(a.b.total_rb, a.H, a.L));
   hipLaunchKernelGGL(kern, grid, dim3(B * 4), lds, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }

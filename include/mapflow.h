@@ -153,10 +153,12 @@ size_t mf_compress_workspace_size(const mf_sender_desc* desc, const mf_batch* ba
  * (l * H_s + h) * total_rowblocks + i:
  *   row_ptr  DEVICE int32 [num_layers * H_s * total_rowblocks + 1]
  *   col_idx  DEVICE int32 [capacity_blocks], ascending within a row
- *   values   DEVICE [capacity_blocks][B][B] in dtype, or NULL (count only):
- *            values[e][r][c] = exp(s_rc - row_lse_r) for query row r and key
- *            column c of the block, exactly the sender's probabilities (not
- *            renormalised), 0 where c is past row r or past the sequence.
+ *   values   DEVICE [capacity_blocks][B][B] in dtype, or NULL (count only),
+ *            key-major: values[e][c][r] = exp(s_rc - row_lse_r) for key
+ *            column c and query row r of the block, exactly the sender's
+ *            probabilities (not renormalised), 0 where c is past row r or
+ *            past the sequence.  Key-major rows let the fused kernel stage a
+ *            block with plain 16-byte copies.
  * nnz_out HOST or NULL.  Non-NULL: the call synchronises `stream`, stores the
  * number of kept blocks, and returns MF_ERR_CAPACITY (row_ptr valid,
  * col_idx/values untouched) when it exceeds capacity_blocks; with col_idx

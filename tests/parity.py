@@ -171,7 +171,8 @@ def check_layer(run: GpuRun, li: int, rowblocks: Optional[Sequence[int]] = None,
                 override[(h, i)] = cols
                 u = orc.compress_unit(q64, k64, rb, h, B, tau, orc.default_scale(wl.d), keep_strip=True)
                 lc.units[(h, i)] = u
-            vals_g = st.values[e0:e1].to(torch.float64).cpu().numpy()
+            # stored key-major: [e][key][query]
+            vals_g = st.values[e0:e1].to(torch.float64).cpu().numpy().transpose(0, 2, 1)
             for t, j in enumerate(cols):
                 want = u.block(int(j), B) if ndiff else u.values[list(u.sel.kept).index(j)]
                 err = np.abs(vals_g[t] - want)
