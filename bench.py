@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rowblocks", type=int, default=48)
+    ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -70,42 +70,38 @@ def measured_traffic(kernel: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, tau, n_rowblocks, layers):
-    """The oracle (as is) on a bounded sample: every sender head of a few
-    row-blocks spread over one layer (stats, selection, extraction), then the
-    mapped output of those row-blocks; extrapolated by causal-pair count to
-    the whole step."""
+def cpu_baseline(wl, tau, n_layers):
+    """The oracle (as is) on a bounded sample: every row-block and sender head
+    of the first `n_layers` layers (stats, selection, extraction, mapped
+    output), extrapolated by layer count to the whole step."""
     from threadpoolctl import threadpool_info
 
     from cross_model_attention_mf_amd import synth
     from oracle import mapflow_oracle as orc
 
-    li = synth.layer_inputs(wl, 0)
     lay = synth.batch_layout(wl)
-    q, k, v = synth.to_f64(li.q), synth.to_f64(li.k), synth.to_f64(li.v)
-    W = li.w.double().numpy()
     rbs = orc.enumerate_rowblocks(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
-    n = len(rbs)
-    pick = sorted({int(x) for x in np.linspace(0, n - 1, n_rowblocks)})
     scale = orc.default_scale(wl.d)
-    t0 = time.perf_counter()
-    for i in pick:
-        rb = rbs[i]
-        kv = []
-        for h in range(wl.H_s):
-            u = orc.compress_unit(q, k, rb, h, wl.B, tau, scale)
-            kv.append((u.sel.kept, u.values))
-        orc.mapped_rowblock(kv, W, v, rb, wl.B)
-    dt = time.perf_counter() - t0
-    pairs = lambda rb: rb.rows * (rb.last_pos + 1)
-    frac = sum(pairs(rbs[i]) for i in pick) / sum(pairs(rb) for rb in rbs)
-    step_s = dt / frac * layers
+    dt = 0.0
+    for layer in range(n_layers):
+        li = synth.layer_inputs(wl, layer, layout=lay)
+        q, k, v = synth.to_f64(li.q), synth.to_f64(li.k), synth.to_f64(li.v)
+        W = li.w.double().numpy()
+        t0 = time.perf_counter()
+        for rb in rbs:
+            kv = []
+            for h in range(wl.H_s):
+                u = orc.compress_unit(q, k, rb, h, wl.B, tau, scale)
+                kv.append((u.sel.kept, u.values))
+            orc.mapped_rowblock(kv, W, v, rb, wl.B)
+        dt += time.perf_counter() - t0
+    step_s = dt / n_layers * wl.num_layers
     threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
     return {"value": round(lay.total_q / step_s, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"layer 0, {len(pick)} of {n} row-blocks x all {wl.H_s} sender heads "
+            "sample": f"layers 0..{n_layers - 1}: all {len(rbs)} row-blocks x all {wl.H_s} sender heads "
                       f"(stats, selection, extraction, mapped output); {dt:.1f} s measured, "
-                      f"extrapolated by causal pairs to {layers} layers"}
+                      f"scaled by layer count to {wl.num_layers} layers"}
 
 
 def main():
@@ -236,7 +232,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, tau, args.cpu_sample_rowblocks, L)
+        res["cpu_baseline"] = cpu_baseline(wl, tau, min(args.cpu_sample_layers, L))
     print(json.dumps(res), flush=True)
 
 
