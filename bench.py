@@ -152,7 +152,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass)
+        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass, st.stats_workspace)
         if ev is not None:
             ev[1].record(stream)
         mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, tau, st.row_ptr,

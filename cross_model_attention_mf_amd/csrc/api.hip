@@ -98,6 +98,13 @@ WorkspaceLayout workspace_layout(const mf_sender_desc* s, const mf_batch* b) {
   return w;
 }
 
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,23 +125,44 @@ const char* mf_last_error_message(void) { return mf::error_buffer(); }
 
 const char* mf_version(void) { return "mapflow-mi355x 0.1"; }
 
+size_t mf_block_stats_workspace_size(const mf_sender_desc* desc, const mf_batch* batch) {
+  if (!desc || !batch) return 0;
+  if (!mf::stats_fast_path(desc->dtype, desc->B, desc->d)) return 0;
+  const int cus = device_cu_count();
+  if (cus <= 0) return 0;
+  return mf::stats_workspace_layout(desc->B, batch->info.max_colblocks, batch->info.total_rowblocks,
+                                    mf::stats_slots(cus)).bytes;
+}
+
 mf_status mf_block_stats(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
-                         float* row_lse, float* block_mass, void* stream) {
+                         float* row_lse, float* block_mass, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   mf::clear_error();
   const char* fn = "mf_block_stats";
   mf_status st = check_sender(desc, batch, fn);
   if (st) return st;
   if (desc->num_layers == 0 || batch->info.total_rowblocks == 0) return MF_OK;
   if (!q || !k || !row_lse || !block_mass) return fail(MF_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
-  const size_t lds = mf::block_stats_lds_bytes(desc->B, batch->info.max_colblocks);
-  if (lds > device_lds_limit())
-    return fail(MF_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed, device allows %zu", fn, lds, device_lds_limit());
   mf::StatsArgs a;
   a.b = batch_args(batch);
   a.q = q; a.k = k; a.row_lse = row_lse; a.block_mass = block_mass;
   a.lsq = desc->layer_stride_q; a.lsk = desc->layer_stride_k;
   a.L = desc->num_layers; a.H = desc->H_s; a.Hkv = desc->H_kv_s; a.d = desc->d; a.B = desc->B;
   a.scale = scale_of(desc);
+  a.ws = nullptr;
+  if (mf::stats_fast_path(desc->dtype, desc->B, desc->d)) {
+    const int cus = device_cu_count();
+    if (cus <= 0) return fail(MF_ERR_HIP, "%s: cannot query the device's compute units", fn);
+    a.wsl = mf::stats_workspace_layout(desc->B, batch->info.max_colblocks, batch->info.total_rowblocks,
+                                       mf::stats_slots(cus));
+    if (!workspace || workspace_bytes < a.wsl.bytes)
+      return fail(MF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, a.wsl.bytes, workspace_bytes);
+    a.ws = workspace;
+  } else {
+    const size_t lds = mf::block_stats_lds_bytes(desc->B, batch->info.max_colblocks);
+    if (lds > device_lds_limit())
+      return fail(MF_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed, device allows %zu", fn, lds, device_lds_limit());
+  }
   const int e = mf::launch_block_stats(a, desc->dtype, stream);
   return e ? hip_fail(e, fn) : MF_OK;
 }

@@ -21,6 +21,11 @@ struct BatchArgs {
   int32_t total_k;
 };
 
+struct StatsWorkspace {
+  size_t hdr, table, escratch, bytes;  // byte offsets inside the workspace
+  int32_t slots;                       // persistent workgroups
+};
+
 struct StatsArgs {
   BatchArgs b;
   const void* q;
@@ -30,6 +35,8 @@ struct StatsArgs {
   int64_t lsq, lsk;        // layer strides (elements)
   int32_t L, H, Hkv, d, B;
   double scale;            // logit scale
+  void* ws;                // MFMA path workspace (null: portable kernel)
+  StatsWorkspace wsl;
 };
 
 struct SelectArgs {
@@ -85,6 +92,9 @@ struct MappedArgs {
 // Launchers: return 0 on success, a hipError_t value otherwise.
 int launch_block_stats(const StatsArgs& a, mf_dtype dt, void* stream);
 size_t block_stats_lds_bytes(int B, int max_cb);
+bool stats_fast_path(mf_dtype dt, int B, int d);
+StatsWorkspace stats_workspace_layout(int B, int max_cb, int total_rb, int slots);
+int stats_slots(int num_cus);
 int launch_select(const SelectArgs& a, void* stream);
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream);

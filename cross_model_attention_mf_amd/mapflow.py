@@ -20,7 +20,8 @@ MF_OK, MF_ERR_INVALID, MF_ERR_UNSUPPORTED, MF_ERR_CAPACITY, MF_ERR_HIP, MF_ERR_W
 MF_F32, MF_BF16 = 0, 1
 MF_MAX_KEYS = 40448
 MF_MAX_LAYERS = 256
-EXPORTS = ("mf_plan", "mf_block_stats", "mf_compress_workspace_size", "mf_compress_blocks",
+EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
+           "mf_compress_workspace_size", "mf_compress_blocks",
            "mf_mapped_attn_v", "mf_status_string", "mf_last_error_message", "mf_version")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -82,7 +83,9 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     L.mf_plan.argtypes = [_i32p, _i32p, _i32p, i32, i32, _i32p, i64, ctypes.POINTER(PlanInfo)]
-    L.mf_block_stats.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp, vp]
+    L.mf_block_stats.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp, vp, sz, vp]
+    L.mf_block_stats_workspace_size.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC)]
+    L.mf_block_stats_workspace_size.restype = sz
     L.mf_compress_workspace_size.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC)]
     L.mf_compress_workspace_size.restype = sz
     L.mf_compress_blocks.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
@@ -176,9 +179,15 @@ def sender_desc(q: torch.Tensor, k: torch.Tensor, B: int, sm_scale: float = 0.0)
                       q[0].numel(), k[0].numel())
 
 
-def block_stats(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, stream=None):
+def block_stats_workspace_size(desc: SenderDesc, batch: Batch) -> int:
+    return int(lib().mf_block_stats_workspace_size(ctypes.byref(desc), ctypes.byref(batch.c)))
+
+
+def block_stats(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().mf_block_stats(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(q), _ptr(k),
-                                _ptr(row_lse), _ptr(block_mass), _stream(stream)))
+                                _ptr(row_lse), _ptr(block_mass), _ptr(workspace), ws_bytes,
+                                _stream(stream)))
 
 
 def compress_workspace_size(desc: SenderDesc, batch: Batch) -> int:

@@ -28,6 +28,7 @@ class SenderState:
     values: torch.Tensor       # [capacity, B, B]
     nnz: Optional[int]
     workspace: torch.Tensor
+    stats_workspace: Optional[torch.Tensor] = None
 
     @property
     def B(self) -> int:
@@ -48,21 +49,23 @@ def alloc_sender(batch: mf.Batch, q: torch.Tensor, k: torch.Tensor, B: int, capa
     col_idx = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
     values = torch.empty((max(capacity, 1), B, B), dtype=q.dtype, device=dev)
     ws = torch.empty(max(mf.compress_workspace_size(desc, batch), 1), dtype=torch.uint8, device=dev)
-    return SenderState(desc, batch, row_lse, block_mass, row_ptr, col_idx, values, None, ws)
+    n_sws = mf.block_stats_workspace_size(desc, batch)
+    sws = torch.empty(n_sws, dtype=torch.uint8, device=dev) if n_sws else None
+    return SenderState(desc, batch, row_lse, block_mass, row_ptr, col_idx, values, None, ws, sws)
 
 
 def count_capacity(batch: mf.Batch, q, k, B: int, tau: float, sm_scale: float = 0.0) -> int:
     """Kept-block count for (q, k, tau): stats + selection with no values (syncs once)."""
     st = alloc_sender(batch, q, k, B, 0, sm_scale)
     qq, kk = (q[None], k[None]) if q.dim() == 3 else (q, k)
-    mf.block_stats(st.desc, batch, qq, kk, st.row_lse, st.block_mass)
+    mf.block_stats(st.desc, batch, qq, kk, st.row_lse, st.block_mass, st.stats_workspace)
     return mf.compress_blocks(st.desc, batch, qq, kk, st.row_lse, st.block_mass, tau, st.row_ptr,
                               None, None, 0, st.workspace, sync_count=True)
 
 
 def compress(st: SenderState, q, k, tau: float, sync_count: bool = True, stream=None) -> SenderState:
     qq, kk = (q[None], k[None]) if q.dim() == 3 else (q, k)
-    mf.block_stats(st.desc, st.batch, qq, kk, st.row_lse, st.block_mass, stream)
+    mf.block_stats(st.desc, st.batch, qq, kk, st.row_lse, st.block_mass, st.stats_workspace, stream)
     st.nnz = mf.compress_blocks(st.desc, st.batch, qq, kk, st.row_lse, st.block_mass, tau,
                                 st.row_ptr, st.col_idx, st.values, st.col_idx.numel(),
                                 st.workspace, sync_count, stream)

@@ -140,7 +140,17 @@ typedef struct {
  * causal column blocks are 0 .. (position of its last row) / B. */
 mf_status mf_block_stats(const mf_sender_desc* desc, const mf_batch* batch,
                          const void* q, const void* k,
-                         float* row_lse, float* block_mass, void* stream);
+                         float* row_lse, float* block_mass,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mf_block_stats needs for this batch on the current device
+ * (0 when the shapes take the path without scratch; then workspace may be
+ * NULL).  workspace: DEVICE, at least this many bytes, owned by the caller;
+ * its contents on entry do not matter and are scratch afterwards (per-block
+ * log masses of the row-blocks in flight, the work queue of the persistent
+ * grid).  Calls that overlap in time need distinct workspaces.  Too small a
+ * workspace returns MF_ERR_WORKSPACE before anything is launched. */
+size_t mf_block_stats_workspace_size(const mf_sender_desc* desc, const mf_batch* batch);
 
 /* Workspace bytes mf_compress_blocks needs for this batch. */
 size_t mf_compress_workspace_size(const mf_sender_desc* desc, const mf_batch* batch);

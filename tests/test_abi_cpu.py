@@ -119,7 +119,7 @@ def _sender(**kw):
 def test_block_stats_validation(kw, status):
     b = _host_batch([0, 256], [0, 256], None, kw.get("B", 64) if kw.get("B", 64) in (32, 64, 128) else 64)
     d = _sender(**kw)
-    st = mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None)
+    st = mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None, 0, None)
     assert st == status, mf.lib().mf_last_error_message()
     assert mf.lib().mf_last_error_message().decode()
 
@@ -127,13 +127,13 @@ def test_block_stats_validation(kw, status):
 def test_block_mismatch_between_plan_and_desc():
     b = _host_batch([0, 256], [0, 256], None, 32)
     d = _sender(B=64)
-    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None) == mf.MF_ERR_INVALID
+    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), 16, 16, 16, 16, None, 0, None) == mf.MF_ERR_INVALID
 
 
 def test_empty_batch_is_a_noop():
     b = _host_batch([0], [0], None, 64)
     d = _sender()
-    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), None, None, None, None, None) == mf.MF_OK
+    assert mf.lib().mf_block_stats(ctypes.byref(d), ctypes.byref(b), None, None, None, None, None, 0, None) == mf.MF_OK
 
 
 @pytest.mark.parametrize("tau", [0.0, -0.5, 1.5, float("nan")])

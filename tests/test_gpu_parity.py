@@ -116,7 +116,7 @@ def test_capacity_sync_and_async():
     nnz = st.nnz
     q = run.inputs[0].q[None].cuda(); k = run.inputs[0].k[None].cuda()
     small = pipeline.alloc_sender(st.batch, q, k, wl.B, nnz - 3)
-    mf.block_stats(small.desc, small.batch, q, k, small.row_lse, small.block_mass)
+    mf.block_stats(small.desc, small.batch, q, k, small.row_lse, small.block_mass, small.stats_workspace)
     with pytest.raises(mf.MapflowError) as e:
         mf.compress_blocks(small.desc, small.batch, q, k, small.row_lse, small.block_mass, 0.8,
                            small.row_ptr, small.col_idx, small.values, nnz - 3, small.workspace)
@@ -167,3 +167,22 @@ def test_portable_and_mfma_mapped_kernels_agree_with_oracle(monkeypatch, B, d, H
         runs.append(run.outs[0].float())
     # both kernels compute the same sums in a different order
     assert torch.allclose(runs[0], runs[1], rtol=2e-2, atol=2e-2 * float(runs[0].abs().max()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_portable_and_mfma_block_stats_agree_with_oracle(monkeypatch, d):
+    # varlen chunked batch: groups of four row-blocks cut short by sequence
+    # ends, a one-row tail block, a sequence shorter than one block, several
+    # (layer, head) pairs per XCD queue, and chunk rows starting past 0
+    wl = tiny_structured("bf16", workload_id=15, B=64, d=d, H_s=12, H_r=4, num_layers=2,
+                         seqlens=(64 * 9 + 17, 64 * 2 + 1, 63, 64 * 5, 700), chunk=256)
+    results = []
+    for portable in ("1", "0"):
+        monkeypatch.setenv("MF_PORTABLE_STATS", portable)
+        run = parity.run_gpu(wl, 0.9, [0, 1], step=1)
+        for li in range(2):
+            parity.check_layer(run, li)
+        results.append((run.state.row_lse.clone(), run.state.block_mass.clone()))
+    (lse_p, mass_p), (lse_f, mass_f) = results
+    assert torch.allclose(lse_p, lse_f, rtol=0, atol=1e-4)
+    assert float((mass_p - mass_f).abs().max()) <= 2e-6
