@@ -12,6 +12,8 @@
 //            blocks only (MFMA), P = exp(S * scale - row_lse), and writes
 //            each B x B block key-major (values[e][key][query]) through LDS
 //            so every store is a full 16-byte vector.
+#include <stdlib.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -211,6 +213,186 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, B = 64: one workgroup of four waves per CSR row.  The row's kept
+// column blocks are listed in LDS; their K tiles stream once through an
+// LDS ring (async global_load_lds, 16-byte chunks XOR-swizzled per key row)
+// shared by the four waves, and wave w computes quadrant (row half w & 1,
+// key half w >> 1) of every block on MFMA 32x32x16 (A = Q rows kept in
+// registers, B = K keys from LDS).  Lane L then holds key 32 kh + L % 32 and
+// the four consecutive rows 8 (e / 4) + 4 (L / 32) + 0..3 of register group
+// e / 4, so exp2(s c2 - lse2) of four rows packs into one 8-byte bf16 LDS
+// write of the key-major tile; the workgroup then stores the 8 KB tile with
+// 16-byte vector stores.
+// ---------------------------------------------------------------------------
+constexpr int XNST = 3;                 // K ring depth
+constexpr int XPITCH = 64 * 2 + 16;     // bytes per key row of the output tile (16-byte aligned)
+constexpr int kXMaxCb = (MF_MAX_KEYS + 63) / 64;   // column blocks of the longest sequence
+
+// Async 16-byte-per-lane copy HBM -> LDS (lane L lands at base + 16 L).
+// Issued as inline assembly so the compiler does not track it: it would
+// otherwise drain every copy in flight (vmcnt(0)) before any later LDS
+// access, including the output tile, which no copy ever writes.  The kernel
+// waits for the copies itself (counted vmcnt) before the barrier that opens
+// a ring slot.  The instruction writes no VGPR.
+__device__ __forceinline__ void xcopy16(const void* gsrc, char* lds_generic_base) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic_base);
+  // one wait state between the M0 write and the copy that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void xwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  const unsigned a = __builtin_bit_cast(unsigned short, (bf16)lo);
+  const unsigned b = __builtin_bit_cast(unsigned short, (bf16)hi);
+  return a | (b << 16);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int STAGE = 64 * ROWB;
+  constexpr int CPW = STAGE / 1024 / 4;
+  constexpr int OT = 64 * XPITCH;       // one output tile
+  // the K ring is the only LDS the async copies write; the output tiles and
+  // the block list are separate objects, so their LDS accesses do not have
+  // to wait for copies in flight
+  extern __shared__ __align__(16) char ring[];
+  __shared__ __align__(16) char otile[2 * OT];
+  __shared__ int jlist[kXMaxCb];
+  __shared__ int nkept;
+
+  int rb, h, l;
+  xcd_unflatten(blockIdx.x, a.b.total_rb, a.H, a.L, rb, h, l);
+  if (l >= a.L) return;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, 64, rb);
+  const size_t lh = (size_t)l * a.H + h;
+  const size_t row = lh * a.b.total_rb + rb;
+  const int64_t base = a.row_ptr[row];
+  const int hk = h / (a.H / a.Hkv);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qh = w & 1, kh = w >> 1;
+
+  // kept column blocks of the row, ascending, and their col_idx entries
+  if (tid == 0) {
+    const uint32_t* __restrict__ kb = a.keep_bits + row * (size_t)a.words;
+    int n = 0;
+    for (int wd = 0; wd < a.words; ++wd) {
+      uint32_t bw = kb[wd];
+      while (bw) {
+        const int j = wd * 32 + __builtin_ctz(bw);
+        bw &= bw - 1;
+        if (base + n < a.capacity) a.col_idx[base + n] = j;
+        jlist[n++] = j;
+      }
+    }
+    const int64_t room = a.capacity - base;
+    nkept = a.values ? (int)(room < 0 ? 0 : (room < n ? room : n)) : 0;
+  }
+  __syncthreads();
+  const int n = nkept;
+  if (n == 0) return;
+
+  const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)l * a.lsk +
+                                   (size_t)ri.k0 * a.Hkv * D + (size_t)hk * D;
+  const size_t kstride = (size_t)a.Hkv * D;
+  const int klast = ri.klen - 1;
+  auto issue = [&](int t) {
+    const int j = jlist[t < n ? t : n - 1];
+    char* stage = ring + (t % XNST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int pidx = (i * 4 + w) * 64 + lane;
+      const int key = pidx / CPR, cc = pidx % CPR;
+      const int src_chunk = cc ^ (key & (CPR - 1));
+      const int kabs = min(j * 64 + key, klast);
+      xcopy16(kbase + (size_t)kabs * kstride + src_chunk * 8, stage + (i * 4 + w) * 1024);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < XNST - 1; ++t) issue(t);
+
+  // Q rows 32 qh + L % 32 as A operands; lse2 of the lane's 16 output rows
+  bf16x8 qf[KS];
+  {
+    const int r = 32 * qh + l32;
+    const bf16* src = reinterpret_cast<const bf16*>(a.q) + (size_t)l * a.lsq +
+                      ((size_t)(ri.q0 + (r < ri.rows ? r : 0)) * a.H + h) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+  }
+  const float c2 = (float)(a.scale * kLog2eD);
+  float lse2[16];
+  {
+    const float* __restrict__ lrow = a.row_lse + lh * a.b.total_q + ri.q0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 32 * qh + 8 * (e >> 2) + 4 * hi + (e & 3);
+      const float v = lrow[r < ri.rows ? r : 0];
+      lse2[e] = r < ri.rows ? v * kLog2e : INFINITY;
+    }
+  }
+  const int diag = ri.ncand - 1;
+  bf16* __restrict__ vals = reinterpret_cast<bf16*>(a.values);
+
+  for (int t = 0; t < n; ++t) {
+    switch (min(t, XNST - 1)) {
+      case 0: xwait_vmcnt<(XNST - 2) * CPW + 0>(); break;
+      case 1: xwait_vmcnt<(XNST - 2) * CPW + 2>(); break;
+      default: xwait_vmcnt<(XNST - 2) * CPW + 4>(); break;
+    }
+    __syncthreads();
+    issue(t + XNST - 1);
+    const char* stage = ring + (t % XNST) * STAGE;
+    f32x16 acc = f32x16{};
+    const int key = 32 * kh + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int chunk = (2 * ks + hi) ^ (key & (CPR - 1));
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + key * ROWB + chunk * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc, 0, 0, 0);
+    }
+    // causal mask (diagonal block only) and rows past the row-block: lse2 = inf
+    const bool dg = jlist[t] == diag;
+    char* ot = otile + (t & 1) * OT;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g + i;
+        const int r = 32 * qh + 8 * g + 4 * hi + i;
+        float x = __builtin_amdgcn_exp2f(fmaf(acc[e], c2, -lse2[e]));
+        if (dg && key > r) x = 0.f;
+        p[i] = x;
+      }
+      const int r0 = 32 * qh + 8 * g + 4 * hi;
+      uint2 pk;
+      pk.x = pack_bf16x2(p[0], p[1]);
+      pk.y = pack_bf16x2(p[2], p[3]);
+      *reinterpret_cast<uint2*>(ot + key * XPITCH + r0 * 2) = pk;
+    }
+    __syncthreads();
+    bf16* dst = vals + (size_t)(base + t) * 64 * 64;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = c * 256 + tid;           // 16-byte chunk: key ch / 8, rows 8 (ch % 8) ..
+      const int kk = ch >> 3, part = ch & 7;
+      *reinterpret_cast<uint4*>(dst + kk * 64 + part * 8) =
+          *reinterpret_cast<const uint4*>(ot + kk * XPITCH + part * 16);
+    }
+  }
+}
+
 template <typename T, int B, int D>
 int launch_ex(const ExtractArgs& a, void* stream) {
   dim3 grid(xcd_grid(a.b.total_rb, a.H, a.L));
@@ -260,8 +442,24 @@ int launch_scan(const ScanArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
+bool extract_fast_path(mf_dtype dt, int B, int d) {
+  if (dt != MF_BF16 || B != 64 || (d != 64 && d != 128)) return false;
+  const char* env = getenv("MF_PORTABLE_EXTRACT");
+  return !(env && env[0] == '1');
+}
+
+size_t extract_mfma_lds_bytes(int d) { return (size_t)XNST * 64 * d * 2; }
+
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
+  if (a.values && extract_fast_path(dt, a.B, a.d)) {
+    const size_t lds = extract_mfma_lds_bytes(a.d);
+    auto kern = a.d == 128 ? extract_mfma_kernel<128> : extract_mfma_kernel<64>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(a.b.total_rb, a.H, a.L)), dim3(256), lds, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+  }
   return dt == MF_BF16 ? launch_ex_d<bf16>(a, stream) : launch_ex_d<float>(a, stream);
 }
 
