@@ -111,26 +111,32 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 //
 //   head mix (MFMA 16x16x32, K = sender heads, W block-diagonal in the key
 //   group):  C_e[(g, r)][q] += sum_h [g == g2] W[r][h] P_h[32cb + 8 g2 + e][q]
-//   so after the 4 stages lane (g, q) holds, for e = 0..7, the mixed map
-//   A_r[q][32cb + 8g + e]: exactly the A operand (8 keys per lane group) of
-//   the P.V MFMA, and the mixed map never leaves registers;
+//   so lane (g, q) holds, for e = 0..7, the mixed map A_r[q][32cb + 8g + e]:
+//   exactly the A operand (8 keys per lane group) of the P.V MFMA, and the
+//   mixed map never leaves registers.  Key groups not yet mixed are still
+//   zero, so P.V runs twice per step, after stages 1 and 3, each time over
+//   the 16 keys whose V rows are in LDS:
 //   P.V (MFMA 16x16x32, K = keys): O_r[q][n] += A_r[q][c] V_r[c][n].
 //
-// Memory pipeline: key-major block rows (RQ contiguous queries) and V rows
-// are copied HBM -> LDS with global_load_lds (16 bytes per lane, no
-// registers); stages are double-buffered, the next stage's copies are issued
-// right after the barrier that opens the current one, and the V rows of a
-// 32-key step are issued at its first stage and used after its last.  The
-// column lists of the sender heads and the page ids of paged values also
-// arrive through async LDS copies, so no register-dependent load drains the
-// pipeline.  Every lane of every copy instruction loads (absent heads and
-// keys past the sequence read a valid row whose finite values meet zero
-// weights or zero probabilities).  Operands are read with ds_read_tr16_b64
-// (lane t of a 16-lane group gets column t of a 4-row tile) from rows whose
-// 16-byte chunks are XOR-swizzled.
+// Memory pipeline: key-major block rows (RQ contiguous queries) are copied
+// HBM -> LDS with global_load_lds (16 bytes per lane, no registers) into a
+// 3-slot ring: the copies of stage s + 2 are issued at stage s, right after
+// the barrier that opens it, so two stages are in flight while one is mixed.
+// The V rows of a 16-key half arrive in their own buffer, issued at the
+// half's first stage and used after its second.  Every stage issues its P
+// copies last and always the same number of them, so a single counted wait
+// (vmcnt = P copies per stage) at the top of each stage covers both the
+// stage's P rows and the half's V rows.  The copies are issued as inline
+// assembly, which the compiler does not track, so it inserts no drain of the
+// ring before LDS accesses; the kernel's own waits and barriers order them.
+// The column lists of the sender heads and the page ids of paged values also
+// arrive through async LDS copies.  Every lane of every copy instruction
+// loads (absent heads and keys past the sequence read a valid row whose
+// finite values meet zero weights or zero probabilities).  Operands are read
+// with ds_read_tr16_b64 (lane t of a 16-lane group gets column t of a 4-row
+// tile) from rows whose 16-byte chunks are XOR-swizzled.
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x4 tr_read(const char* lds_generic, unsigned byte_off) {
   auto p = (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)
@@ -139,11 +145,24 @@ __device__ __forceinline__ bf16x4 tr_read(const char* lds_generic, unsigned byte
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Async copies HBM -> LDS; lane L lands at base + size * L.  Inline assembly
+// (one wait state between the M0 write and the copy reading it); the copy
+// writes no VGPR.
 __device__ __forceinline__ void async_copy16(const void* gsrc, char* lds_generic_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)((uintptr_t)lds_generic_base), 16, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(base)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void async_copy4(const void* gsrc, char* lds_generic_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)((uintptr_t)lds_generic_base), 4, 0, 0);
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(gsrc), "s"(base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // A copy of a lane value the compiler cannot see through: per-stage address
@@ -174,28 +193,38 @@ struct MapCfg {
   static constexpr int NW = 2 * NQT;                   // waves
   static constexpr int NT = D / 16;                    // 16-wide n tiles of d
   static constexpr int CB = B / 32;                    // 32-key steps per block
+  static constexpr int SPU = 4 * CB;                   // 8-key stages per block
   static constexpr int QH = B / RQ;                    // workgroups per row-block
   static constexpr int PROW = RQ * 2;                  // bytes per P row (one key, RQ queries)
   static constexpr int PCPR = PROW / 16;               // 16-byte chunks per P row
   static constexpr int VROW = D * 2;                   // bytes per V row
   static constexpr int VCPR = VROW / 16;
-  static constexpr int VBYTES = 8 * 32 * VROW;         // 8 heads x 32 keys
+  static constexpr int VBYTES = 8 * 16 * VROW;         // 8 heads x 16 keys
   static constexpr int HPAD = 8 * HP8;
   static constexpr int SBYTES = 8 * HPAD * PROW;       // one stage: 8 keys x all heads
+  static constexpr int NSLOT = 3;                      // P ring slots
+  static constexpr int AHEAD = NSLOT - 1;              // stages issued ahead of the mix
   static constexpr int PI = SBYTES / 1024;             // copy instructions per stage
-  static constexpr int VI = VBYTES / 1024;             // copy instructions per step for V
+  static constexpr int PW = PI / NW;                   // ... per wave
+  static constexpr int VI = VBYTES / 1024;             // copy instructions per half step for V
+  static_assert(PI % NW == 0, "P copies must split evenly over the waves");
+  static_assert(VI % NW == 0, "V copies must split evenly over the waves");
 };
 
 size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
   const int hpad = (Hs + 7) / 8 * 8;
   const int RQ = B < 64 ? B : 64;
   const size_t stage = (size_t)8 * hpad * RQ * 2;
-  const size_t vbytes = (size_t)8 * 32 * D * 2;
-  const size_t obytes = (size_t)RQ * 8 * D * 2;       // output staging (aliases the stages and V)
-  size_t main = 2 * stage + vbytes;
+  const size_t vbytes = (size_t)8 * 16 * D * 2;
+  const size_t obytes = (size_t)RQ * 8 * D * 2;       // output staging (aliases the ring and V)
+  size_t main = 3 * stage + vbytes;
   if (obytes > main) main = obytes;
   return main + 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
 }
+
+// column of an exhausted sender head (the merge copies it instead of a
+// col_idx entry)
+__device__ const int kNoColumn = 0x7FFFFFFF;
 
 template <int B, int D, int HP8>
 __global__ void __launch_bounds__(((B < 64 ? B : 64) / 16) * 2 * 64)
@@ -203,9 +232,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   using C = MapCfg<B, D, HP8>;
   constexpr int hpad = C::HPAD;
   extern __shared__ __align__(16) char smem[];
-  char* stages = smem;
-  char* Vs = smem + 2 * C::SBYTES;
-  size_t main_bytes = 2 * C::SBYTES + C::VBYTES;
+  char* ring = smem;
+  char* Vs = smem + C::NSLOT * C::SBYTES;
+  size_t main_bytes = C::NSLOT * C::SBYTES + C::VBYTES;
   if ((size_t)C::RQ * 8 * D * 2 > main_bytes) main_bytes = (size_t)C::RQ * 8 * D * 2;
   UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + main_bytes);
   int* curcol = reinterpret_cast<int*>(UI + 2);        // next column of each sender head
@@ -232,7 +261,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   const int lg = lane >> 4, lr = lane & 15;
   const bool paged = a.block_table != nullptr;
 
-  // ---- zero the stages and V rows, load the group's W rows
+  // ---- zero the ring and V rows, load the group's W rows
   for (size_t o = (size_t)tid * 16; o < main_bytes; o += (size_t)C::NW * 64 * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
   for (int t = tid; t < 8 * 64; t += C::NW * 64) {
@@ -264,9 +293,11 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     if (take) {
       out->vidx[lane] = (int)mptr;
       ++mptr;
-      if (mptr < mend) async_copy4(a.col_idx + mptr, reinterpret_cast<char*>(curcol));
-      else curcol[lane] = 0x7FFFFFFF;
     }
+    // every lane copies: the next column of a head that advanced, its current
+    // column otherwise, the sentinel once its list is exhausted
+    const int* src = mptr < mend ? a.col_idx + mptr : &kNoColumn;
+    async_copy4(src, reinterpret_cast<char*>(curcol));
     if (lane == 0) { out->j = jm; out->mask = m; }
     if (paged && jm != 0x7FFFFFFF) {
       for (int k0 = 0; k0 < B; k0 += 64) {
@@ -278,39 +309,45 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   };
   __syncthreads();
   if (wave == 0) merge(&UI[0]);
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_vmcnt<0>();
   __syncthreads();
 
   const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
   const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)l * a.lsv;
 
-  // stage (union info, step cb, key group g2): keys 32cb + 8 g2 + e of all
-  // heads -> stage buffer; row 8h + e holds RQ queries of head h, key e
-  auto issue_p = [&](const UnionInfo* ui, int cb, int g2, char* buf) {
+  // stage (union info, stage si of the block) -> ring slot: keys 8 si + e of
+  // all heads; row 8h + e holds RQ queries of head h, key e.  ui == nullptr
+  // issues the same number of copies from a valid dummy row.
+  auto issue_p = [&](const UnionInfo* ui, int si, char* buf) {
     constexpr int RPI = 1024 / C::PROW;                // rows per copy instruction
-    const unsigned long long mk = ui->mask;
+    const unsigned long long mk = ui ? ui->mask : 0ull;
     const int ln = opaque(lane);
-    for (int k = wave; k < C::PI; k += C::NW) {
+#pragma unroll 1
+    for (int i = 0; i < C::PW; ++i) {
+      const int k = wave + i * C::NW;
       const int rho = k * RPI + ln / C::PCPR;
       const int p = ln % C::PCPR;
       const int h = rho >> 3, e = rho & 7;
       const int lc = p ^ swz(rho, C::PCPR);
       const bool live = h < a.Hs && ((mk >> h) & 1ull);
-      const bf16* src = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)(32 * cb + 8 * g2 + e) * B + qoff + 8 * lc
+      const bf16* src = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)(8 * si + e) * B + qoff + 8 * lc
                              : vals + 8 * lc;
       async_copy16(src, buf + (size_t)k * 1024);
     }
   };
-  // V rows of a 32-key step for the group's 8 receiver heads -> Vs
-  auto issue_v = [&](const UnionInfo* ui, int cb) {
+  // V rows of 16-key half hh of the block for the group's 8 receiver heads
+  // -> Vs, row 16 r_local + key
+  auto issue_v = [&](const UnionInfo* ui, int hh) {
     constexpr int RPI = 1024 / C::VROW;
     const int ln = opaque(lane);
-    for (int k = wave; k < C::VI; k += C::NW) {
-      const int rho = k * RPI + ln / C::VCPR;          // row = r_local * 32 + c_local
+#pragma unroll 1
+    for (int i = 0; i < C::VI / C::NW; ++i) {
+      const int k = wave + i * C::NW;
+      const int rho = k * RPI + ln / C::VCPR;
       const int p = ln % C::VCPR;
-      const int rl = rho / 32, cl = rho % 32;
+      const int rl = rho >> 4, cl = rho & 15;
       const int r = 8 * grp + rl;
-      const int kl = 32 * cb + cl;                     // key inside the block
+      const int kl = 16 * hh + cl;                     // key inside the block
       const int key = ui->j * B + kl;
       const bool live = r < a.Hr && key < ri.klen;
       const int g = live ? r / (a.Hr / a.Hkv) : 0;
@@ -333,47 +370,54 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) O[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane transpose-read offsets inside a stage buffer: rows 8h + e of the
+  // per-lane transpose-read offsets inside a ring slot: rows 8h + e of the
   // lane's 4-head group (two reads: heads 8lg + (lr>>2) and + 4), columns q
   const int q = 16 * qt + 4 * (lr & 3);
   const int plc = q >> 3, pwithin = (q & 7) * 2;
   const float* wrow = Wsh + (4 * hq + (lr & 3)) * 64;
 
   if (UI[0].j != 0x7FFFFFFF) {
-    issue_p(&UI[0], 0, 0, stages);
-    int u = 0, cb = 0, g2 = 0, s = 0;
+    // stages are numbered over the whole walk: stage s is stage s % SPU of
+    // union block s / SPU; issue runs two stages ahead of the mix
+    issue_p(&UI[0], 0, ring);
+    issue_p(&UI[0], 1, ring + C::SBYTES);
     bf16x8 Wk[2];
     f32x4 Cacc[8];
-    for (;;) {
-      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0;; ++s) {
+      // P rows of stage s and the V rows of its half have landed (only the
+      // P copies issued at stage s - 1 may still be in flight)
+      wait_vmcnt<C::PW>();
       __syncthreads();
+      const int u = s / C::SPU, si = s % C::SPU;
       const UnionInfo* ui = &UI[u & 1];
-      if (g2 == 0) {
-        if (cb == 0) {
-          if (wave == 0) merge(&UI[(u + 1) & 1]);
-          // W of this union block: sender heads that do not keep j get weight 0
-          const unsigned long long mk = ui->mask;
+      if (si == 0 && ui->j == 0x7FFFFFFF) break;
+      const int g2 = si & 3;
+      if (si == 0) {
+        if (wave == 0) merge(&UI[(u + 1) & 1]);
+        // W of this union block: sender heads that do not keep j get weight 0
+        const unsigned long long mk = ui->mask;
 #pragma unroll
-          for (int hk = 0; hk < 2; ++hk)
+        for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
-            for (int ee = 0; ee < 8; ++ee) {
-              const int h = 32 * hk + 8 * lg + ee;
-              Wk[hk][ee] = (bf16)(((mk >> h) & 1ull) ? wrow[h] : 0.f);
-            }
-        }
-        issue_v(ui, cb);
-#pragma unroll
-        for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int ee = 0; ee < 8; ++ee) {
+            const int h = 32 * hk + 8 * lg + ee;
+            Wk[hk][ee] = (bf16)(((mk >> h) & 1ull) ? wrow[h] : 0.f);
+          }
       }
-      // ---- issue the next stage (if any) into the other buffer
-      int nu = u, ncb = cb, ng2 = g2 + 1;
-      if (ng2 == 4) { ng2 = 0; if (++ncb == C::CB) { ncb = 0; ++nu; } }
-      const bool more = (nu == u) || UI[nu & 1].j != 0x7FFFFFFF;
-      if (more) issue_p(&UI[nu & 1], ncb, ng2, stages + (size_t)((s + 1) & 1) * C::SBYTES);
+      if ((g2 & 1) == 0) issue_v(ui, si >> 1);
+      // ---- P copies of stage s + 2 (dummy rows past the last block)
+      {
+        const int s2 = s + 2, u2 = s2 / C::SPU;
+        const UnionInfo* ui2 = &UI[u2 & 1];
+        const bool real = u2 == u || ui2->j != 0x7FFFFFFF;
+        issue_p(real ? ui2 : nullptr, s2 % C::SPU, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
+      }
 
       // ---- head mix over the 8 keys of key group g2: lanes of key group g2
       // take W, the others zero (block-diagonal)
-      const char* cur = stages + (size_t)(s & 1) * C::SBYTES;
+      const char* cur = ring + (size_t)(s % C::NSLOT) * C::SBYTES;
       const bf16x8 zero8 = {};
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
@@ -396,8 +440,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
           }
         }
       }
-      if (g2 == 3) {
-        // ---- P.V for this 32-key step: A_r[q][32cb + 8lg + e] = Cacc[e][i]
+      if (g2 & 1) {
+        // ---- P.V over the 16 keys of this half: A_r[q][32cb + 8lg + e] =
+        // Cacc[e][i]; lane groups of the other half hold zeros, and their V
+        // rows (any finite row of the buffer) add nothing
         bf16x8 Aop[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -406,7 +452,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         const int nlo = 4 * (lr & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rho0 = (4 * hq + i) * 32 + 8 * lg + (lr >> 2);
+          const int rho0 = (4 * hq + i) * 16 + 8 * (lg & 1) + (lr >> 2);
           const int sw0 = swz(rho0, C::VCPR);           // same for rho0 + 4
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) {
@@ -419,14 +465,14 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
             O[i][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[i], vop, O[i][nt], 0, 0, 0);
           }
         }
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      if (!more) break;
-      u = nu; cb = ncb; g2 = ng2; ++s;
     }
   }
 
   // ---- output: stage [q][8 heads][d] in LDS, then 16-byte stores of whole rows
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_vmcnt<0>();
   __syncthreads();
   bf16* stage = reinterpret_cast<bf16*>(smem);
 #pragma unroll
