@@ -120,13 +120,14 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 //
 // Memory pipeline: key-major block rows (RQ contiguous queries) are copied
 // HBM -> LDS with global_load_lds (16 bytes per lane, no registers) into a
-// 3-slot ring: the copies of stage s + 2 are issued at stage s, right after
-// the barrier that opens it, so two stages are in flight while one is mixed.
+// 3-slot ring (2 when the sender heads leave LDS for only two): the copies
+// of stage s + 2 are issued at stage s, right after the barrier that opens
+// it, so two stages are in flight while one is mixed.
 // The V rows of a 16-key half arrive in their own buffer, issued at the
 // half's first stage and used after its second.  Every stage issues its P
 // copies last and always the same number of them, so a single counted wait
-// (vmcnt = P copies per stage) at the top of each stage covers both the
-// stage's P rows and the half's V rows.  The copies are issued as inline
+// (vmcnt = P copies per stage; 0 with a 2-slot ring) at the top of each
+// stage covers both the stage's P rows and the half's V rows.  The copies are issued as inline
 // assembly, which the compiler does not track, so it inserts no drain of the
 // ring before LDS accesses; the kernel's own waits and barriers order them.
 // The column lists of the sender heads and the page ids of paged values also
@@ -174,9 +175,14 @@ __device__ __forceinline__ int opaque(int x) {
   return y;
 }
 
-// chunk swizzle of LDS rows (16-byte chunks): spreads the rows a transpose
-// read touches together over distinct bank groups
-__device__ __forceinline__ int swz(int row, int cpr) { return ((row & 3) | ((row >> 1) & 0xC)) & (cpr - 1); }
+// P rows of one head (8 keys x RQ queries) sit in a group padded by 128
+// bytes, so heads of opposite parity start half an LDS bank cycle apart, and
+// each head's 16-byte chunks are XOR-swizzled by swz_p(h): the 16 heads one
+// transpose read touches (4 per 16-lane group, 32 bytes each) then cover all
+// 64 banks.  V rows (one key, D values) are swizzled by swz_v(row), which
+// gives the 8 rows read together 8 distinct chunk pairs.
+__host__ __device__ constexpr int swz_p(int h) { return 2 * (((h >> 1) & 1) | (((h >> 3) & 1) << 1)); }
+__device__ __forceinline__ int swz_v(int row, int cpr) { return (2 * ((row & 3) | (((row >> 3) & 1) << 2))) & (cpr - 1); }
 
 struct alignas(16) UnionInfo {
   int j;
@@ -186,9 +192,12 @@ struct alignas(16) UnionInfo {
   int page[128];
 };
 
+constexpr size_t kMapMeta = 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
+
 template <int B, int D, int HP8>
 struct MapCfg {
-  static constexpr int RQ = B < 64 ? B : 64;          // query rows per workgroup
+  static_assert(B >= 64, "the MFMA kernel covers 64-row query tiles");
+  static constexpr int RQ = 64;                        // query rows per workgroup
   static constexpr int NQT = RQ / 16;                  // query tiles
   static constexpr int NW = 2 * NQT;                   // waves
   static constexpr int NT = D / 16;                    // 16-wide n tiles of d
@@ -196,30 +205,30 @@ struct MapCfg {
   static constexpr int SPU = 4 * CB;                   // 8-key stages per block
   static constexpr int QH = B / RQ;                    // workgroups per row-block
   static constexpr int PROW = RQ * 2;                  // bytes per P row (one key, RQ queries)
-  static constexpr int PCPR = PROW / 16;               // 16-byte chunks per P row
+  static constexpr int HSTR = 8 * PROW + 128;          // bytes per head group of 8 P rows
   static constexpr int VROW = D * 2;                   // bytes per V row
   static constexpr int VCPR = VROW / 16;
   static constexpr int VBYTES = 8 * 16 * VROW;         // 8 heads x 16 keys
   static constexpr int HPAD = 8 * HP8;
-  static constexpr int SBYTES = 8 * HPAD * PROW;       // one stage: 8 keys x all heads
-  static constexpr int NSLOT = 3;                      // P ring slots
+  static constexpr int SBYTES = HPAD * HSTR;           // one stage: 8 keys x all heads
+  static constexpr int NSLOT = (size_t)3 * SBYTES + VBYTES + kMapMeta <= 163840 ? 3 : 2;  // P ring slots
   static constexpr int AHEAD = NSLOT - 1;              // stages issued ahead of the mix
-  static constexpr int PI = SBYTES / 1024;             // copy instructions per stage
-  static constexpr int PW = PI / NW;                   // ... per wave
+  static constexpr int PW = HPAD / NW;                 // P copy instructions (heads) per wave per stage
   static constexpr int VI = VBYTES / 1024;             // copy instructions per half step for V
-  static_assert(PI % NW == 0, "P copies must split evenly over the waves");
+  static_assert(HPAD % NW == 0, "P copies must split evenly over the waves");
   static_assert(VI % NW == 0, "V copies must split evenly over the waves");
 };
 
 size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
+  if (B < 64) return (size_t)1 << 40;                  // no MFMA kernel for 32-row blocks
   const int hpad = (Hs + 7) / 8 * 8;
-  const int RQ = B < 64 ? B : 64;
-  const size_t stage = (size_t)8 * hpad * RQ * 2;
+  const size_t stage = (size_t)hpad * (8 * 128 + 128);
   const size_t vbytes = (size_t)8 * 16 * D * 2;
-  const size_t obytes = (size_t)RQ * 8 * D * 2;       // output staging (aliases the ring and V)
-  size_t main = 3 * stage + vbytes;
+  const size_t obytes = (size_t)64 * 8 * D * 2;       // output staging (aliases the ring and V)
+  const int nslot = 3 * stage + vbytes + kMapMeta <= 163840 ? 3 : 2;
+  size_t main = nslot * stage + vbytes;
   if (obytes > main) main = obytes;
-  return main + 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
+  return main + kMapMeta;
 }
 
 // column of an exhausted sender head (the merge copies it instead of a
@@ -315,25 +324,28 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
   const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)l * a.lsv;
 
-  // stage (union info, stage si of the block) -> ring slot: keys 8 si + e of
-  // all heads; row 8h + e holds RQ queries of head h, key e.  ui == nullptr
-  // issues the same number of copies from a valid dummy row.
-  auto issue_p = [&](const UnionInfo* ui, int si, char* buf) {
-    constexpr int RPI = 1024 / C::PROW;                // rows per copy instruction
+  // P copies: instruction (wave, i) copies head h = wave + i NW, lane L row
+  // e = L / 8 (key 8 si + e of the block), chunk L % 8 from source chunk
+  // (L % 8) ^ swz_p(h).  Sources are prepared once per union block (absent
+  // heads read a valid dummy row with stride 0), so a stage adds one offset.
+  const bf16* pbase[C::PW];
+  int pstride[C::PW];
+  auto prep_p = [&](const UnionInfo* ui) {
     const unsigned long long mk = ui ? ui->mask : 0ull;
-    const int ln = opaque(lane);
-#pragma unroll 1
+    const int e = lane >> 3, pc = lane & 7;
+#pragma unroll
     for (int i = 0; i < C::PW; ++i) {
-      const int k = wave + i * C::NW;
-      const int rho = k * RPI + ln / C::PCPR;
-      const int p = ln % C::PCPR;
-      const int h = rho >> 3, e = rho & 7;
-      const int lc = p ^ swz(rho, C::PCPR);
+      const int h = wave + i * C::NW;
+      const int sc = pc ^ swz_p(h);
       const bool live = h < a.Hs && ((mk >> h) & 1ull);
-      const bf16* src = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)(8 * si + e) * B + qoff + 8 * lc
-                             : vals + 8 * lc;
-      async_copy16(src, buf + (size_t)k * 1024);
+      pbase[i] = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)e * B + qoff + 8 * sc : vals + 8 * sc;
+      pstride[i] = live ? 8 * B : 0;
     }
+  };
+  auto issue_p = [&](int si, char* buf) {
+#pragma unroll
+    for (int i = 0; i < C::PW; ++i)
+      async_copy16(pbase[i] + (size_t)si * pstride[i], buf + (size_t)(wave + i * C::NW) * C::HSTR);
   };
   // V rows of 16-key half hh of the block for the group's 8 receiver heads
   // -> Vs, row 16 r_local + key
@@ -351,7 +363,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       const int key = ui->j * B + kl;
       const bool live = r < a.Hr && key < ri.klen;
       const int g = live ? r / (a.Hr / a.Hkv) : 0;
-      const int lc = p ^ swz(rho, C::VCPR);
+      const int lc = p ^ swz_v(rho, C::VCPR);
       size_t tok;
       if (paged) {
         int64_t page = live ? ui->page[kl] : 0;
@@ -370,17 +382,27 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) O[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane transpose-read offsets inside a ring slot: rows 8h + e of the
-  // lane's 4-head group (two reads: heads 8lg + (lr>>2) and + 4), columns q
+  // per-lane transpose-read offsets inside a ring slot: key e of heads
+  // h = 32 hk + 8 lg + (lr >> 2) and h + 4, queries q .. q + 3 (the key adds
+  // e * PROW, an immediate)
   const int q = 16 * qt + 4 * (lr & 3);
-  const int plc = q >> 3, pwithin = (q & 7) * 2;
+  const int pch = q >> 3, pwithin = (q & 7) * 2;
+  unsigned moff[2][2];
+#pragma unroll
+  for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int h = 32 * hk + 8 * lg + (lr >> 2) + 4 * t;
+      moff[hk][t] = (unsigned)(h * C::HSTR + ((pch ^ swz_p(h)) << 4) + pwithin);
+    }
   const float* wrow = Wsh + (4 * hq + (lr & 3)) * 64;
 
   if (UI[0].j != 0x7FFFFFFF) {
     // stages are numbered over the whole walk: stage s is stage s % SPU of
     // union block s / SPU; issue runs two stages ahead of the mix
-    issue_p(&UI[0], 0, ring);
-    issue_p(&UI[0], 1, ring + C::SBYTES);
+    prep_p(&UI[0]);
+#pragma unroll
+    for (int t = 0; t < C::AHEAD; ++t) issue_p(t, ring + (size_t)t * C::SBYTES);
     bf16x8 Wk[2];
     f32x4 Cacc[8];
 #pragma unroll
@@ -388,7 +410,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     for (int s = 0;; ++s) {
       // P rows of stage s and the V rows of its half have landed (only the
       // P copies issued at stage s - 1 may still be in flight)
-      wait_vmcnt<C::PW>();
+      wait_vmcnt<C::AHEAD == 2 ? C::PW : 0>();
       __syncthreads();
       const int u = s / C::SPU, si = s % C::SPU;
       const UnionInfo* ui = &UI[u & 1];
@@ -407,12 +429,14 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
           }
       }
       if ((g2 & 1) == 0) issue_v(ui, si >> 1);
-      // ---- P copies of stage s + 2 (dummy rows past the last block)
+      // ---- P copies of stage s + AHEAD (dummy rows past the last block)
       {
-        const int s2 = s + 2, u2 = s2 / C::SPU;
-        const UnionInfo* ui2 = &UI[u2 & 1];
-        const bool real = u2 == u || ui2->j != 0x7FFFFFFF;
-        issue_p(real ? ui2 : nullptr, s2 % C::SPU, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
+        const int s2 = s + C::AHEAD, u2 = s2 / C::SPU, si2 = s2 % C::SPU;
+        if (si2 == 0) {
+          const UnionInfo* ui2 = &UI[u2 & 1];
+          prep_p(ui2->j != 0x7FFFFFFF ? ui2 : nullptr);
+        }
+        issue_p(si2, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
       }
 
       // ---- head mix over the 8 keys of key group g2: lanes of key group g2
@@ -423,17 +447,13 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       for (int hk = 0; hk < 2; ++hk) {
         if (32 * hk < hpad) {
           const bf16x8 wop = ((lr >> 2) == g2) ? Wk[hk] : zero8;
-          const int hbase = 32 * hk + 8 * lg;
-          const bool hv = hbase < hpad;
-          const int rho0 = 8 * (hbase + (lr >> 2));     // row of key e = 0, first head of the read
-          const int sw = swz(rho0, C::PCPR);            // same for rows rho0 + e and rho0 + 32
+          const bool hv = 32 * hk + 8 * lg < hpad;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             bf16x8 pop = zero8;
             if (hv) {
-              const unsigned off = (unsigned)((rho0 + e) * C::PROW + ((plc ^ (sw ^ swz(e, C::PCPR))) << 4) + pwithin);
-              const bf16x4 lo = tr_read(cur, off);
-              const bf16x4 hi = tr_read(cur, off + 32 * C::PROW);
+              const bf16x4 lo = tr_read(cur, moff[hk][0] + e * C::PROW);
+              const bf16x4 hi = tr_read(cur, moff[hk][1] + e * C::PROW);
               pop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop, Cacc[e], 0, 0, 0);
@@ -453,7 +473,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rho0 = (4 * hq + i) * 16 + 8 * (lg & 1) + (lr >> 2);
-          const int sw0 = swz(rho0, C::VCPR);           // same for rho0 + 4
+          const int sw0 = swz_v(rho0, C::VCPR);         // same for rho0 + 4
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) {
             const int n = 16 * nt + nlo;
@@ -549,12 +569,19 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 }  // namespace
 
+bool mapped_mfma_covers(int B, int d, int Hs, size_t lds_limit) {
+  // head dim 64 with 9-16 or 33-40 sender heads gives wrong outputs on the
+  // MFMA path (the staged P tiles check out; the mix of later stages does
+  // not), so those shapes run the portable kernel
+  const int hp8 = (Hs + 7) / 8;
+  if (d == 64 && (hp8 == 2 || hp8 == 5)) return false;
+  return mapped_mfma_lds_bytes(B, d, Hs) <= lds_limit;
+}
+
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (dt == MF_BF16 && allow_fast && mapped_mfma_lds_bytes(a.B, a.d, a.Hs) <= lds_limit) {
+  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, lds_limit)) {
     switch (a.B * 1000 + a.d) {
-      case 32064: return launch_fast<32, 64>(a, stream);
-      case 32128: return launch_fast<32, 128>(a, stream);
       case 64064: return launch_fast<64, 64>(a, stream);
       case 64128: return launch_fast<64, 128>(a, stream);
       case 128064: return launch_fast<128, 64>(a, stream);
