@@ -305,16 +305,32 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
 
     // copies of column block jtop - t into ring slot t % SNST (steps past the
     // end re-read block 0 so every wave issues the same number of copies)
+    // copy slot i of this wave: key kkey[i] of the block, source chunk
+    // csrc[i]; its source for block jb is kptr[i] + jb * 64 rows
+    const bf16* kptr[CPW];
+    int kkey[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int pidx = (i * SQ + w) * 64 + lane;  // 16-byte chunk index in the stage
+      const int key = pidx / CPR, cc = pidx % CPR;
+      const int src_chunk = cc ^ (key & (CPR - 1));
+      kkey[i] = key;
+      kptr[i] = kbase + (size_t)key * kstride + src_chunk * 8;
+    }
     auto issue = [&](int t) {
       const int jb = max(jtop - t, 0);
       char* stage = smem + (t % SNST) * STAGE;
+      if (jb * 64 + 63 <= klast) {
+        const size_t step = (size_t)jb * 64 * kstride;
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int pidx = (i * SQ + w) * 64 + lane;  // 16-byte chunk index in the stage
-        const int key = pidx / CPR, cc = pidx % CPR;
-        const int src_chunk = cc ^ (key & (CPR - 1));
-        const int kabs = min(jb * 64 + key, klast);
-        copy16_to_lds(kbase + (size_t)kabs * kstride + src_chunk * 8, stage + (i * SQ + w) * 1024);
+        for (int i = 0; i < CPW; ++i) copy16_to_lds(kptr[i] + step, stage + (i * SQ + w) * 1024);
+      } else {
+        // block reaching past the last key: clamp rows to the last key
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+          const int over = max(jb * 64 + kkey[i] - klast, 0);
+          copy16_to_lds(kptr[i] + ((size_t)jb * 64 - over) * kstride, stage + (i * SQ + w) * 1024);
+        }
       }
     };
 #pragma unroll
@@ -413,14 +429,16 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
             s1 += __builtin_amdgcn_exp2f(fmaf(acc[1][qt][e], c2, -nb));
           }
           const float s = swap32_sum(s0 + s1);
+          // s is in [1, 64]: the hardware log2 is exact to an ulp there
+          const float ls = __builtin_amdgcn_logf(s);
           if (first) {
             m_ref[qt] = m_new;
             l_run[qt] = (double)s;
-            evq[qt] = log2f(s);
+            evq[qt] = ls;
           } else {
-            if (m_new > m_run[qt]) l_run[qt] *= (double)exp2f((m_run[qt] - m_new) * c2);
-            l_run[qt] += (double)s;
-            evq[qt] = log2f(s) + (float)(((double)m_new - (double)m_ref[qt]) * c2d);
+            // exp2(0) is exactly 1, so an unchanged maximum leaves l_run as is
+            l_run[qt] = l_run[qt] * (double)__builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2) + (double)s;
+            evq[qt] = ls + (float)(((double)m_new - (double)m_ref[qt]) * c2d);
           }
           m_run[qt] = m_new;
         }
