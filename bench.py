@@ -31,9 +31,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = {
-    "block_stats_kernel": "cross_model_attention_mf_amd/csrc/k_stats.hip",
-    "mapped": "cross_model_attention_mf_amd/csrc/k_mapped.hip",
-    "extract_kernel": "cross_model_attention_mf_amd/csrc/k_compress.hip",
+    "stats_mfma_kernel": "cross_model_attention_mf_amd/csrc/k_stats.hip",
+    "mapped_mfma_kernel": "cross_model_attention_mf_amd/csrc/k_mapped.hip",
+    "extract_mfma_kernel": "cross_model_attention_mf_amd/csrc/k_compress.hip",
 }
 
 
@@ -189,17 +189,17 @@ def main():
     stats_tflops = stats_flops / t_stats / 1e12
     map_gbs = map_bytes / t_map / 1e9
     rooflines = {
-        "block_stats_kernel": {"bound": "mfma", "achieved": round(stats_tflops, 2),
+        "stats_mfma_kernel": {"bound": "mfma", "achieved": round(stats_tflops, 2),
                                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(stats_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                               "traffic": measured_traffic("block_stats_kernel"),
+                               "traffic": measured_traffic("stats_mfma_kernel"),
                                "us_per_launch": round(t_stats * 1e6, 1)},
-        "mapped": {"bound": "hbm", "achieved": round(map_gbs, 1), "peak": HBM_PEAK_GBS,
+        "mapped_mfma_kernel": {"bound": "hbm", "achieved": round(map_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(map_gbs / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic("mapped"),
+                   "traffic": measured_traffic("mapped_mfma_kernel"),
                    "us_per_launch": round(t_map * 1e6, 1)},
     }
-    dominant = max(("block_stats_kernel", t_stats), ("mapped", t_map), key=lambda x: x[1])[0]
+    dominant = max(("stats_mfma_kernel", t_stats), ("mapped_mfma_kernel", t_map), key=lambda x: x[1])[0]
     res = {
         "metric": "mapped-attn·V GB/s & % HBM peak; block-compress tokens/s at 8K ctx",
         "value": round(N / (ms_per_step * 1e-3), 1),
