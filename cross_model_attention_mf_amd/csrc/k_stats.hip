@@ -178,9 +178,12 @@ int launch_d(const StatsArgs& a, void* stream) {
 // highest diagonal block down to block 0; a wave joins at its own diagonal,
 // which is therefore its first block and sets m_ref, as in the portable
 // kernel.  Scores are computed transposed, S^T = K Q^T: lane L then holds
-// query L % 32 of each 32-query half and 16 keys of each 32-key tile, so the
+// query L % 32 of each 32-query half and 16 keys of each 32-key tile, so a
 // row max / row sum over a 64-key block is an in-lane reduction plus one
-// v_permlane32_swap with lane L ^ 32.  Each block's log2 mass relative to
+// v_permlane32_swap with lane L ^ 32.  Only the diagonal block takes a row
+// max: it is the exponent reference of every later block of the row, whose
+// sums are taken against it directly (a block that would overflow that
+// reference is re-taken against its own maximum).  Each block's log2 mass relative to
 // m_ref goes to a per-slot scratch table in HBM ([block][row], one coalesced
 // 256-byte store per wave and block); the epilogue reads it back through LDS
 // transposes and sums the masses in fp64.  The grid is persistent: slot b
@@ -394,8 +397,28 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
           kf0 = kf1;
           kf1 = kf2;
         }
-        const bool first = jb == diag;
-        if (first) {
+        // per row: its sum over the block relative to the reference m_run,
+        // both 32-key halves (in-lane) and both lane halves (one swap)
+        auto block_sum = [&](int qt, float nb) {
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            s0 += __builtin_amdgcn_exp2f(fmaf(acc[0][qt][e], c2, -nb));
+            s1 += __builtin_amdgcn_exp2f(fmaf(acc[1][qt][e], c2, -nb));
+          }
+          return swap32_sum(s0 + s1);
+        };
+        auto block_max = [&](int qt) {
+          float mx = acc[0][qt][0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[0][qt][e]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[1][qt][e]);
+          return swap32_max(mx);
+        };
+        float evq[2];
+        if (jb == diag) {
+          asm volatile("");  // a real branch: this runs once per row-block
           // causal mask inside the diagonal block, key index > query index:
           // tile (kt = 1, qt = 0) lies wholly above the diagonal, (0, 1)
           // wholly below; in the two diagonal tiles register e holds key
@@ -410,37 +433,41 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
             acc[1][1][e] = masked ? -INFINITY : acc[1][1][e];
             acc[1][0][e] = -INFINITY;
           }
-        }
-        float evq[2];
+          // the diagonal block's maximum is the reference of the row's
+          // log2 masses; s lies in [1, 64], where the hardware log2 is
+          // exact to an ulp
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          float mx = acc[0][qt][0];
-#pragma unroll
-          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[0][qt][e]);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[1][qt][e]);
-          mx = swap32_max(mx);
-          const float m_new = first ? mx : fmaxf(m_run[qt], mx);
-          const float nb = m_new * c2;
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            s0 += __builtin_amdgcn_exp2f(fmaf(acc[0][qt][e], c2, -nb));
-            s1 += __builtin_amdgcn_exp2f(fmaf(acc[1][qt][e], c2, -nb));
-          }
-          const float s = swap32_sum(s0 + s1);
-          // s is in [1, 64]: the hardware log2 is exact to an ulp there
-          const float ls = __builtin_amdgcn_logf(s);
-          if (first) {
-            m_ref[qt] = m_new;
+          for (int qt = 0; qt < 2; ++qt) {
+            const float mx = block_max(qt);
+            const float s = block_sum(qt, mx * c2);
+            m_ref[qt] = m_run[qt] = mx;
             l_run[qt] = (double)s;
-            evq[qt] = ls;
-          } else {
-            // exp2(0) is exactly 1, so an unchanged maximum leaves l_run as is
-            l_run[qt] = l_run[qt] * (double)__builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2) + (double)s;
-            evq[qt] = ls + (float)(((double)m_new - (double)m_ref[qt]) * c2d);
+            evq[qt] = __builtin_amdgcn_logf(s);
           }
-          m_run[qt] = m_new;
+        } else {
+          // Off the diagonal the exponent reference stays m_run; no block
+          // maximum is needed unless a score exceeds it so far that the
+          // sum leaves [0, 2^64) (overflow, or NaN from an infinite score).
+          // Then the wave re-takes the block with its maximum folded in.
+          float s[2];
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) s[qt] = block_sum(qt, m_run[qt] * c2);
+          const bool big = !(s[0] < 0x1p64f) || !(s[1] < 0x1p64f);
+          if (__builtin_expect(__ballot(big) != 0, 0)) {
+            asm volatile("");
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+              const float m_new = fmaxf(m_run[qt], block_max(qt));
+              l_run[qt] *= (double)__builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
+              m_run[qt] = m_new;
+              s[qt] = block_sum(qt, m_new * c2);
+            }
+          }
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            l_run[qt] += (double)s[qt];
+            evq[qt] = __builtin_amdgcn_logf(s[qt]) + (float)(((double)m_run[qt] - (double)m_ref[qt]) * c2d);
+          }
         }
         ev = hi ? evq[1] : evq[0];
       }
@@ -462,10 +489,15 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       float* __restrict__ bm = a.block_mass + (lh * a.b.total_rb + rb) * (size_t)a.b.max_cb;
       for (int j0 = 0; j0 < ri.ncand; j0 += 64) {
         const int nj = min(64, ri.ncand - j0);
-        for (int jj = 0; jj < nj; ++jj) {
-          const float e = __hip_atomic_load(ew + (size_t)(j0 + jj) * 64 + lane, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-          tr[jj * SEPITCH + lane] = lane < ri.rows ? exp2f((float)((double)e - lse2)) : 0.f;
+        // the scratch rows were written by this wave on this CU and its
+        // stores have completed: plain loads see them.  Eight in flight.
+        for (int jj = 0; jj < nj; jj += 8) {
+          float e[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = ew[(size_t)min(j0 + jj + u, ri.ncand - 1) * 64 + lane];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (jj + u < nj) tr[(jj + u) * SEPITCH + lane] = lane < ri.rows ? exp2f((float)((double)e[u] - lse2)) : 0.f;
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         if (lane < nj) {
