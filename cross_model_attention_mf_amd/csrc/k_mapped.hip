@@ -124,16 +124,20 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 // of stage s + 2 are issued at stage s, right after the barrier that opens
 // it, so two stages are in flight while one is mixed.
 // The V rows of a 16-key half arrive in their own buffer, issued at the
-// half's first stage and used after its second.  Every stage issues its P
-// copies last and always the same number of them, so a single counted wait
-// (vmcnt = P copies per stage; 0 with a 2-slot ring) at the top of each
-// stage covers both the stage's P rows and the half's V rows.  The copies are issued as inline
+// half's first stage and used after its second; they are staged once per
+// value head the group's receiver heads read (grouped-query receivers share
+// them), not once per receiver head.  Only sender heads that keep the block
+// issue P copies; the slot of an absent head keeps finite values from an
+// earlier block (or the initial zeros), which meet a zero weight.  Every
+// stage issues its P copies last, so one counted wait at the top of each
+// stage (vmcnt = the wave's P copies of the previous stage, a wave-uniform
+// count; 0 with a 2-slot ring) covers both the stage's P rows and the
+// half's V rows.  The copies are issued as inline
 // assembly, which the compiler does not track, so it inserts no drain of the
 // ring before LDS accesses; the kernel's own waits and barriers order them.
 // The column lists of the sender heads and the page ids of paged values also
-// arrive through async LDS copies.  Every lane of every copy instruction
-// loads (absent heads and keys past the sequence read a valid row whose
-// finite values meet zero weights or zero probabilities).  Operands are read
+// arrive through async LDS copies.  Keys past the sequence read a valid row
+// whose finite values meet zero probabilities.  Operands are read
 // with ds_read_tr16_b64 (lane t of a 16-lane group gets column t of a 4-row
 // tile) from rows whose 16-byte chunks are XOR-swizzled.
 // ---------------------------------------------------------------------------
@@ -164,6 +168,23 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// wait until at most n (wave-uniform, 0 <= n <= M) vector memory operations
+// of this wave are outstanding
+template <int M>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  static_assert(M <= 8, "wait range");
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    default: wait_vmcnt<M>(); break;
+  }
 }
 
 // A copy of a lane value the compiler cannot see through: per-stage address
@@ -214,9 +235,9 @@ struct MapCfg {
   static constexpr int NSLOT = (size_t)3 * SBYTES + VBYTES + kMapMeta <= 163840 ? 3 : 2;  // P ring slots
   static constexpr int AHEAD = NSLOT - 1;              // stages issued ahead of the mix
   static constexpr int PW = HPAD / NW;                 // P copy instructions (heads) per wave per stage
-  static constexpr int VI = VBYTES / 1024;             // copy instructions per half step for V
+  static constexpr int RPI = 1024 / VROW;              // V rows per copy instruction
   static_assert(HPAD % NW == 0, "P copies must split evenly over the waves");
-  static_assert(VI % NW == 0, "V copies must split evenly over the waves");
+  static_assert(16 % RPI == 0, "a value head's 16 rows fill whole copy instructions");
 };
 
 size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
@@ -326,43 +347,53 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 
   // P copies: instruction (wave, i) copies head h = wave + i NW, lane L row
   // e = L / 8 (key 8 si + e of the block), chunk L % 8 from source chunk
-  // (L % 8) ^ swz_p(h).  Sources are prepared once per union block (absent
-  // heads read a valid dummy row with stride 0), so a stage adds one offset.
+  // (L % 8) ^ swz_p(h).  Sources are prepared once per union block, so a
+  // stage adds one offset.  Heads that do not keep the block issue no copy:
+  // their slot keeps an earlier block's finite values (or the initial
+  // zeros), which meet a zero weight in the head mix.
   const bf16* pbase[C::PW];
-  int pstride[C::PW];
+  unsigned plive = 0;   // bit i: copy slot i of this wave reads a kept block
+  int p_issued = 0;     // P copies of this wave in the latest issue_p
   auto prep_p = [&](const UnionInfo* ui) {
     const unsigned long long mk = ui ? ui->mask : 0ull;
     const int e = lane >> 3, pc = lane & 7;
+    unsigned bits = 0;
 #pragma unroll
     for (int i = 0; i < C::PW; ++i) {
       const int h = wave + i * C::NW;
       const int sc = pc ^ swz_p(h);
       const bool live = h < a.Hs && ((mk >> h) & 1ull);
-      pbase[i] = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)e * B + qoff + 8 * sc : vals + 8 * sc;
-      pstride[i] = live ? 8 * B : 0;
+      pbase[i] = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)e * B + qoff + 8 * sc : vals;
+      bits |= live ? 1u << i : 0u;
     }
+    plive = __builtin_amdgcn_readfirstlane(bits);
   };
   auto issue_p = [&](int si, char* buf) {
 #pragma unroll
     for (int i = 0; i < C::PW; ++i)
-      async_copy16(pbase[i] + (size_t)si * pstride[i], buf + (size_t)(wave + i * C::NW) * C::HSTR);
+      if ((plive >> i) & 1u)
+        async_copy16(pbase[i] + (size_t)si * 8 * B, buf + (size_t)(wave + i * C::NW) * C::HSTR);
+    p_issued = __builtin_popcount(plive);
   };
-  // V rows of 16-key half hh of the block for the group's 8 receiver heads
-  // -> Vs, row 16 r_local + key
+  // The group's receiver heads read nkv consecutive value heads kv0 ..
+  // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
+  // V rows of 16-key half hh of the block, staged once per value head ->
+  // Vs, row 16 kvl + key
+  const int ratio = a.Hr / a.Hkv;
+  const int kv0 = (8 * grp) / ratio;
+  const int nkv = min(8 * grp + 7, a.Hr - 1) / ratio - kv0 + 1;
   auto issue_v = [&](const UnionInfo* ui, int hh) {
-    constexpr int RPI = 1024 / C::VROW;
     const int ln = opaque(lane);
+    const int ninst = nkv * (16 / C::RPI);
 #pragma unroll 1
-    for (int i = 0; i < C::VI / C::NW; ++i) {
-      const int k = wave + i * C::NW;
-      const int rho = k * RPI + ln / C::VCPR;
+    for (int k = wave; k < ninst; k += C::NW) {
+      const int rho = k * C::RPI + ln / C::VCPR;
       const int p = ln % C::VCPR;
-      const int rl = rho >> 4, cl = rho & 15;
-      const int r = 8 * grp + rl;
+      const int kvl = rho >> 4, cl = rho & 15;
       const int kl = 16 * hh + cl;                     // key inside the block
       const int key = ui->j * B + kl;
-      const bool live = r < a.Hr && key < ri.klen;
-      const int g = live ? r / (a.Hr / a.Hkv) : 0;
+      const bool live = key < ri.klen;
+      const int g = kv0 + kvl;
       const int lc = p ^ swz_v(rho, C::VCPR);
       size_t tok;
       if (paged) {
@@ -409,8 +440,13 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0;; ++s) {
       // P rows of stage s and the V rows of its half have landed (only the
-      // P copies issued at stage s - 1 may still be in flight)
-      wait_vmcnt<C::AHEAD == 2 ? C::PW : 0>();
+      // P copies issued at stage s - 1, the wave's latest, may still be in
+      // flight)
+      if (C::AHEAD == 2) {
+        wait_vmcnt_upto<C::PW>(p_issued);
+      } else {
+        wait_vmcnt<0>();
+      }
       __syncthreads();
       const int u = s / C::SPU, si = s % C::SPU;
       const UnionInfo* ui = &UI[u & 1];
@@ -448,16 +484,20 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         if (32 * hk < hpad) {
           const bf16x8 wop = ((lr >> 2) == g2) ? Wk[hk] : zero8;
           const bool hv = 32 * hk + 8 * lg < hpad;
+          // all eight operands first, then the MFMAs
+          bf16x8 pop[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            bf16x8 pop = zero8;
+            pop[e] = zero8;
             if (hv) {
               const bf16x4 lo = tr_read(cur, moff[hk][0] + e * C::PROW);
               const bf16x4 hi = tr_read(cur, moff[hk][1] + e * C::PROW);
-              pop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+              pop[e] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop, Cacc[e], 0, 0, 0);
           }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop[e], Cacc[e], 0, 0, 0);
         }
       }
       if (g2 & 1) {
@@ -472,7 +512,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         const int nlo = 4 * (lr & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rho0 = (4 * hq + i) * 16 + 8 * (lg & 1) + (lr >> 2);
+          // value head of receiver 8 grp + 4 hq + i, local to the group (a
+          // padding receiver past Hr reads some staged row: its mixed map is 0)
+          const int kvl = min((8 * grp + 4 * hq + i) / ratio - kv0, 7);
+          const int rho0 = kvl * 16 + 8 * (lg & 1) + (lr >> 2);
           const int sw0 = swz_v(rho0, C::VCPR);         // same for rho0 + 4
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) {
