@@ -173,8 +173,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // of this wave are outstanding
 template <int M>
 __device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  static_assert(M <= 8, "wait range");
-  switch (n) {
+  static_assert(M <= 15, "wait range");
+  switch (n < M ? n : M) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<1>(); break;
     case 2: wait_vmcnt<2>(); break;
@@ -183,6 +183,13 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
     case 5: wait_vmcnt<5>(); break;
     case 6: wait_vmcnt<6>(); break;
     case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
     default: wait_vmcnt<M>(); break;
   }
 }
@@ -215,7 +222,7 @@ struct alignas(16) UnionInfo {
 
 constexpr size_t kMapMeta = 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
 
-template <int B, int D, int HP8>
+template <int B, int D, int HP8, int KVC>
 struct MapCfg {
   static_assert(B >= 64, "the MFMA kernel covers 64-row query tiles");
   static constexpr int RQ = 64;                        // query rows per workgroup
@@ -229,10 +236,13 @@ struct MapCfg {
   static constexpr int HSTR = 8 * PROW + 128;          // bytes per head group of 8 P rows
   static constexpr int VROW = D * 2;                   // bytes per V row
   static constexpr int VCPR = VROW / 16;
-  static constexpr int VBYTES = 8 * 16 * VROW;         // 8 heads x 16 keys
+  static constexpr int VB = KVC * 16 * VROW;           // one V buffer: KVC value heads x 16 keys
   static constexpr int HPAD = 8 * HP8;
   static constexpr int SBYTES = HPAD * HSTR;           // one stage: 8 keys x all heads
-  static constexpr int NSLOT = (size_t)3 * SBYTES + VBYTES + kMapMeta <= 163840 ? 3 : 2;  // P ring slots
+  static constexpr bool fits(int ns, int nv) { return (size_t)ns * SBYTES + (size_t)nv * VB + kMapMeta <= 163840; }
+  static constexpr int NSLOT = fits(3, 2) || fits(3, 1) ? 3 : 2;  // P ring slots
+  static constexpr int NVB = fits(NSLOT, 2) ? 2 : 1;   // V buffers
+  static constexpr int VBYTES = NVB * VB;
   static constexpr int AHEAD = NSLOT - 1;              // stages issued ahead of the mix
   static constexpr int PW = HPAD / NW;                 // P copy instructions (heads) per wave per stage
   static constexpr int RPI = 1024 / VROW;              // V rows per copy instruction
@@ -240,14 +250,28 @@ struct MapCfg {
   static_assert(16 % RPI == 0, "a value head's 16 rows fill whole copy instructions");
 };
 
-size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
+// value heads one group of 8 receiver heads reads, at most over the groups
+int group_value_heads(int Hr, int Hkv) {
+  const int ratio = Hr / Hkv;
+  int mx = 0;
+  for (int r0 = 0; r0 < Hr; r0 += 8) {
+    const int r1 = r0 + 7 < Hr - 1 ? r0 + 7 : Hr - 1;
+    const int n = r1 / ratio - r0 / ratio + 1;
+    mx = n > mx ? n : mx;
+  }
+  return mx;
+}
+
+size_t mapped_mfma_lds_bytes(int B, int D, int Hs, int kvc) {
   if (B < 64) return (size_t)1 << 40;                  // no MFMA kernel for 32-row blocks
-  const int hpad = (Hs + 7) / 8 * 8;
-  const size_t stage = (size_t)hpad * (8 * 128 + 128);
-  const size_t vbytes = (size_t)8 * 16 * D * 2;
+  const size_t hpad = (size_t)(Hs + 7) / 8 * 8;
+  const size_t stage = hpad * (8 * 128 + 128);
+  const size_t vb = (size_t)kvc * 16 * D * 2;
+  auto fits = [&](size_t ns, size_t nv) { return ns * stage + nv * vb + kMapMeta <= 163840; };
+  const size_t nslot = fits(3, 2) || fits(3, 1) ? 3 : 2;
+  const size_t nvb = fits(nslot, 2) ? 2 : 1;
   const size_t obytes = (size_t)64 * 8 * D * 2;       // output staging (aliases the ring and V)
-  const int nslot = 3 * stage + vbytes + kMapMeta <= 163840 ? 3 : 2;
-  size_t main = nslot * stage + vbytes;
+  size_t main = nslot * stage + nvb * vb;
   if (obytes > main) main = obytes;
   return main + kMapMeta;
 }
@@ -256,10 +280,10 @@ size_t mapped_mfma_lds_bytes(int B, int D, int Hs) {
 // col_idx entry)
 __device__ const int kNoColumn = 0x7FFFFFFF;
 
-template <int B, int D, int HP8>
+template <int B, int D, int HP8, int KVC>
 __global__ void __launch_bounds__(((B < 64 ? B : 64) / 16) * 2 * 64)
 mapped_mfma_kernel(MappedArgs a, int ngroups) {
-  using C = MapCfg<B, D, HP8>;
+  using C = MapCfg<B, D, HP8, KVC>;
   constexpr int hpad = C::HPAD;
   extern __shared__ __align__(16) char smem[];
   char* ring = smem;
@@ -314,6 +338,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // wave 0: next block of the union and the heads that keep it; the heads'
   // next columns and the block's page ids arrive asynchronously in LDS
   auto merge = [&](UnionInfo* out) {
+    int copies = 1;
     const int mcur = curcol[lane];
     int jm = mcur;
 #pragma unroll
@@ -334,8 +359,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         const int key = min(jm * B + k0 + lane, ri.klen - 1);
         async_copy4(a.block_table + (size_t)ri.seq * a.max_pages + key / a.page_size,
                     reinterpret_cast<char*>(out->page + k0));
+        ++copies;
       }
     }
+    return copies;
   };
   __syncthreads();
   if (wave == 0) merge(&UI[0]);
@@ -353,7 +380,6 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // zeros), which meet a zero weight in the head mix.
   const bf16* pbase[C::PW];
   unsigned plive = 0;   // bit i: copy slot i of this wave reads a kept block
-  int p_issued = 0;     // P copies of this wave in the latest issue_p
   auto prep_p = [&](const UnionInfo* ui) {
     const unsigned long long mk = ui ? ui->mask : 0ull;
     const int e = lane >> 3, pc = lane & 7;
@@ -373,7 +399,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     for (int i = 0; i < C::PW; ++i)
       if ((plive >> i) & 1u)
         async_copy16(pbase[i] + (size_t)si * 8 * B, buf + (size_t)(wave + i * C::NW) * C::HSTR);
-    p_issued = __builtin_popcount(plive);
+    return __builtin_popcount(plive);
   };
   // The group's receiver heads read nkv consecutive value heads kv0 ..
   // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
@@ -382,9 +408,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   const int ratio = a.Hr / a.Hkv;
   const int kv0 = (8 * grp) / ratio;
   const int nkv = min(8 * grp + 7, a.Hr - 1) / ratio - kv0 + 1;
-  auto issue_v = [&](const UnionInfo* ui, int hh) {
+  auto issue_v = [&](const UnionInfo* ui, int hh, int buf) {
     const int ln = opaque(lane);
     const int ninst = nkv * (16 / C::RPI);
+    char* vdst = Vs + (size_t)buf * C::VB;
 #pragma unroll 1
     for (int k = wave; k < ninst; k += C::NW) {
       const int rho = k * C::RPI + ln / C::VCPR;
@@ -403,8 +430,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       } else {
         tok = (size_t)ri.k0 + (live ? key : 0);
       }
-      async_copy16(vbase + (tok * a.Hkv + g) * D + 8 * lc, Vs + (size_t)k * 1024);
+      async_copy16(vbase + (tok * a.Hkv + g) * D + 8 * lc, vdst + (size_t)k * 1024);
     }
+    return wave < ninst ? (ninst - 1 - wave) / C::NW + 1 : 0;
   };
 
   f32x4 O[4][C::NT];
@@ -431,9 +459,19 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   if (UI[0].j != 0x7FFFFFFF) {
     // stages are numbered over the whole walk: stage s is stage s % SPU of
     // union block s / SPU; issue runs two stages ahead of the mix
+    // Copies outstanding at the top of a stage: with two V buffers every copy
+    // is needed two stages after the one that issued it at the earliest, so
+    // all of the previous stage's copies may still be in flight.  With one
+    // V buffer the V rows issued at a half's first stage (and the merge's
+    // copies, issued before them) are needed at its second, so only the
+    // previous stage's P copies, always its last, may be.  With a 2-slot
+    // ring everything is waited for.
+    int ops_prev = 0, p_prev = 0;
     prep_p(&UI[0]);
+    if (C::NVB == 2) issue_v(&UI[0], 0, 0);
 #pragma unroll
-    for (int t = 0; t < C::AHEAD; ++t) issue_p(t, ring + (size_t)t * C::SBYTES);
+    for (int t = 0; t < C::AHEAD; ++t) p_prev = issue_p(t, ring + (size_t)t * C::SBYTES);
+    ops_prev = p_prev;
     bf16x8 Wk[2];
     f32x4 Cacc[8];
 #pragma unroll
@@ -442,18 +480,21 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       // P rows of stage s and the V rows of its half have landed (only the
       // P copies issued at stage s - 1, the wave's latest, may still be in
       // flight)
-      if (C::AHEAD == 2) {
-        wait_vmcnt_upto<C::PW>(p_issued);
-      } else {
+      if (C::AHEAD == 1) {
         wait_vmcnt<0>();
+      } else if (C::NVB == 1) {
+        wait_vmcnt_upto<C::PW>(p_prev);
+      } else {
+        wait_vmcnt_upto<15>(ops_prev);
       }
       __syncthreads();
       const int u = s / C::SPU, si = s % C::SPU;
       const UnionInfo* ui = &UI[u & 1];
       if (si == 0 && ui->j == 0x7FFFFFFF) break;
       const int g2 = si & 3;
+      int ops = 0;
       if (si == 0) {
-        if (wave == 0) merge(&UI[(u + 1) & 1]);
+        if (wave == 0) ops += merge(&UI[(u + 1) & 1]);
         // W of this union block: sender heads that do not keep j get weight 0
         const unsigned long long mk = ui->mask;
 #pragma unroll
@@ -464,7 +505,20 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
             Wk[hk][ee] = (bf16)(((mk >> h) & 1ull) ? wrow[h] : 0.f);
           }
       }
-      if ((g2 & 1) == 0) issue_v(ui, si >> 1);
+      // V rows: with two buffers, those of the next half at the last stage of
+      // this one (into the other buffer); with one, those of this half at
+      // its first stage
+      if (C::NVB == 2) {
+        if (g2 & 1) {
+          const int s1 = s + 1;
+          const UnionInfo* ui1 = &UI[(s1 / C::SPU) & 1];
+          if (ui1->j != 0x7FFFFFFF) {
+            ops += issue_v(ui1, (s1 % C::SPU) >> 1, (s1 >> 1) & 1);
+          }
+        }
+      } else if ((g2 & 1) == 0) {
+        ops += issue_v(ui, si >> 1, 0);
+      }
       // ---- P copies of stage s + AHEAD (dummy rows past the last block)
       {
         const int s2 = s + C::AHEAD, u2 = s2 / C::SPU, si2 = s2 % C::SPU;
@@ -472,8 +526,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
           const UnionInfo* ui2 = &UI[u2 & 1];
           prep_p(ui2->j != 0x7FFFFFFF ? ui2 : nullptr);
         }
-        issue_p(si2, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
+        p_prev = issue_p(si2, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
+        ops += p_prev;
       }
+      ops_prev = ops;
 
       // ---- head mix over the 8 keys of key group g2: lanes of key group g2
       // take W, the others zero (block-diagonal)
@@ -484,16 +540,20 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         if (32 * hk < hpad) {
           const bf16x8 wop = ((lr >> 2) == g2) ? Wk[hk] : zero8;
           const bool hv = 32 * hk + 8 * lg < hpad;
+          // A transposing read gives each lane data from rows other lanes
+          // address, so it never runs under a partial exec mask: every lane
+          // reads (lanes past the padded heads at head 0's rows) and the
+          // lanes past the heads take zeros afterwards.
+          const unsigned o0 = hv ? moff[hk][0] : moff[0][0];
+          const unsigned o1 = hv ? moff[hk][1] : moff[0][1];
           // all eight operands first, then the MFMAs
           bf16x8 pop[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pop[e] = zero8;
-            if (hv) {
-              const bf16x4 lo = tr_read(cur, moff[hk][0] + e * C::PROW);
-              const bf16x4 hi = tr_read(cur, moff[hk][1] + e * C::PROW);
-              pop[e] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
+            const bf16x4 lo = tr_read(cur, o0 + e * C::PROW);
+            const bf16x4 hi = tr_read(cur, o1 + e * C::PROW);
+            const bf16x8 pv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            pop[e] = hv ? pv : zero8;
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -510,11 +570,12 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
           for (int ee = 0; ee < 8; ++ee) Aop[i][ee] = (bf16)Cacc[ee][i];
         const int nlo = 4 * (lr & 3);
+        const char* Vh = Vs + (size_t)(C::NVB == 2 ? (s >> 1) & 1 : 0) * C::VB;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // value head of receiver 8 grp + 4 hq + i, local to the group (a
           // padding receiver past Hr reads some staged row: its mixed map is 0)
-          const int kvl = min((8 * grp + 4 * hq + i) / ratio - kv0, 7);
+          const int kvl = min((8 * grp + 4 * hq + i) / ratio - kv0, KVC - 1);
           const int rho0 = kvl * 16 + 8 * (lg & 1) + (lr >> 2);
           const int sw0 = swz_v(rho0, C::VCPR);         // same for rho0 + 4
 #pragma unroll
@@ -522,8 +583,8 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
             const int n = 16 * nt + nlo;
             const int lc = n >> 3, within = (n & 7) * 2;
             const unsigned off = (unsigned)(rho0 * C::VROW + ((lc ^ sw0) << 4) + within);
-            const bf16x4 lo = tr_read(Vs, off);
-            const bf16x4 hi = tr_read(Vs, off + 4 * C::VROW);
+            const bf16x4 lo = tr_read(Vh, off);
+            const bf16x4 hi = tr_read(Vh, off + 4 * C::VROW);
             const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             O[i][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[i], vop, O[i][nt], 0, 0, 0);
           }
@@ -561,11 +622,11 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   }
 }
 
-template <int B, int D, int HP8>
+template <int B, int D, int HP8, int KVC>
 int launch_fast_h(const MappedArgs& a, void* stream) {
-  using C = MapCfg<B, D, HP8>;
-  const size_t lds = mapped_mfma_lds_bytes(B, D, a.Hs);
-  auto kern = mapped_mfma_kernel<B, D, HP8>;
+  using C = MapCfg<B, D, HP8, KVC>;
+  const size_t lds = mapped_mfma_lds_bytes(B, D, a.Hs, KVC);
+  auto kern = mapped_mfma_kernel<B, D, HP8, KVC>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;
   const int ngroups = (a.Hr + 7) / 8;
@@ -575,19 +636,26 @@ int launch_fast_h(const MappedArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-template <int B, int D>
-int launch_fast(const MappedArgs& a, void* stream) {
+template <int B, int D, int KVC>
+int launch_fast_k(const MappedArgs& a, void* stream) {
   switch ((a.Hs + 7) / 8) {
-    case 1: return launch_fast_h<B, D, 1>(a, stream);
-    case 2: return launch_fast_h<B, D, 2>(a, stream);
-    case 3: return launch_fast_h<B, D, 3>(a, stream);
-    case 4: return launch_fast_h<B, D, 4>(a, stream);
-    case 5: return launch_fast_h<B, D, 5>(a, stream);
-    case 6: return launch_fast_h<B, D, 6>(a, stream);
-    case 7: return launch_fast_h<B, D, 7>(a, stream);
-    case 8: return launch_fast_h<B, D, 8>(a, stream);
+    case 1: return launch_fast_h<B, D, 1, KVC>(a, stream);
+    case 2: return launch_fast_h<B, D, 2, KVC>(a, stream);
+    case 3: return launch_fast_h<B, D, 3, KVC>(a, stream);
+    case 4: return launch_fast_h<B, D, 4, KVC>(a, stream);
+    case 5: return launch_fast_h<B, D, 5, KVC>(a, stream);
+    case 6: return launch_fast_h<B, D, 6, KVC>(a, stream);
+    case 7: return launch_fast_h<B, D, 7, KVC>(a, stream);
+    case 8: return launch_fast_h<B, D, 8, KVC>(a, stream);
   }
   return (int)hipErrorInvalidValue;
+}
+
+// V buffers sized for 4 value heads per group when the grouped-query
+// layout allows, else for 8
+template <int B, int D>
+int launch_fast(const MappedArgs& a, void* stream) {
+  return group_value_heads(a.Hr, a.Hkv) <= 4 ? launch_fast_k<B, D, 4>(a, stream) : launch_fast_k<B, D, 8>(a, stream);
 }
 
 template <typename T, int B, int D>
@@ -612,18 +680,13 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 }  // namespace
 
-bool mapped_mfma_covers(int B, int d, int Hs, size_t lds_limit) {
-  // head dim 64 with 9-16 or 33-40 sender heads gives wrong outputs on the
-  // MFMA path (the staged P tiles check out; the mix of later stages does
-  // not), so those shapes run the portable kernel
-  const int hp8 = (Hs + 7) / 8;
-  if (d == 64 && (hp8 == 2 || hp8 == 5)) return false;
-  return mapped_mfma_lds_bytes(B, d, Hs) <= lds_limit;
+bool mapped_mfma_covers(int B, int d, int Hs, int Hr, int Hkv, size_t lds_limit) {
+  return mapped_mfma_lds_bytes(B, d, Hs, group_value_heads(Hr, Hkv) <= 4 ? 4 : 8) <= lds_limit;
 }
 
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, lds_limit)) {
+  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, a.Hr, a.Hkv, lds_limit)) {
     switch (a.B * 1000 + a.d) {
       case 64064: return launch_fast<64, 64>(a, stream);
       case 64128: return launch_fast<64, 128>(a, stream);
