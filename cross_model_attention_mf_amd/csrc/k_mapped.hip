@@ -294,18 +294,21 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   int* curcol = reinterpret_cast<int*>(UI + 2);        // next column of each sender head
   float* Wsh = reinterpret_cast<float*>(curcol + 64);   // [8 receiver heads][64 sender heads]
 
-  // ---- work item (XCD-aware: the head groups of one row-block share an XCD)
+  // ---- work item.  A unit is one (row-block part, receiver layer); its head
+  // groups run back to back on one XCD (workgroup b runs on XCD b % 8), so
+  // they share that XCD's L2 for the kept values.  Units are dealt to the
+  // XCDs in turn, latest row-blocks first: a row-block's union (and work)
+  // grows with its causal range, and the short ones then fill the tail.
   const int nitems = a.b.total_rb * C::QH;
   int item, grp, l;
   {
-    const long long n = (long long)nitems * ngroups * a.L;
-    const long long per = (n + kXcds - 1) / kXcds;
-    const long long w = (long long)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (w >= n) return;
-    grp = (int)(w % ngroups);
-    const long long t = w / ngroups;
-    item = (int)(t % nitems);
-    l = (int)(t / nitems);
+    const long long nu = (long long)nitems * a.L;
+    const long long pos = blockIdx.x / kXcds;
+    const long long u = (long long)(blockIdx.x % kXcds) + (long long)kXcds * (pos / ngroups);
+    if (u >= nu) return;
+    grp = (int)(pos % ngroups);
+    item = nitems - 1 - (int)(u / a.L);
+    l = (int)(u % a.L);
   }
   const int rb = item / C::QH, qoff = (item % C::QH) * C::RQ;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
@@ -630,9 +633,9 @@ int launch_fast_h(const MappedArgs& a, void* stream) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;
   const int ngroups = (a.Hr + 7) / 8;
-  const long long n = (long long)a.b.total_rb * C::QH * ngroups * a.L;
-  const long long per = (n + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(per * kXcds)), dim3(C::NW * 64), lds, (hipStream_t)stream, a, ngroups);
+  const long long nu = (long long)a.b.total_rb * C::QH * a.L;
+  const long long per_xcd = (nu + kXcds - 1) / kXcds * ngroups;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::NW * 64), lds, (hipStream_t)stream, a, ngroups);
   return (int)hipGetLastError();
 }
 
