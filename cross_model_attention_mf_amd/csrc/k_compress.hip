@@ -225,6 +225,7 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
 // write of the key-major tile; the workgroup then stores the 8 KB tile with
 // 16-byte vector stores.
 // ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int XNST = 3;                 // K ring depth
 constexpr int XPITCH = 64 * 2 + 16;     // bytes per key row of the output tile (16-byte aligned)
 constexpr int kXMaxCb = (MF_MAX_KEYS + 63) / 64;   // column blocks of the longest sequence
@@ -282,21 +283,52 @@ __global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int qh = w & 1, kh = w >> 1;
 
-  // kept column blocks of the row, ascending, and their col_idx entries
-  if (tid == 0) {
-    const uint32_t* __restrict__ kb = a.keep_bits + row * (size_t)a.words;
-    int n = 0;
-    for (int wd = 0; wd < a.words; ++wd) {
-      uint32_t bw = kb[wd];
-      while (bw) {
-        const int j = wd * 32 + __builtin_ctz(bw);
-        bw &= bw - 1;
-        if (base + n < a.capacity) a.col_idx[base + n] = j;
-        jlist[n++] = j;
-      }
+  // Q rows 32 qh + L % 32 as A operands and lse2 of the lane's 16 output
+  // rows: independent of the kept set, so their loads go out first
+  bf16x8 qf[KS];
+  {
+    const int r = 32 * qh + l32;
+    const bf16* src = reinterpret_cast<const bf16*>(a.q) + (size_t)l * a.lsq +
+                      ((size_t)(ri.q0 + (r < ri.rows ? r : 0)) * a.H + h) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+  }
+  const float c2 = (float)(a.scale * kLog2eD);
+  float lse2[16];
+  {
+    const float* __restrict__ lrow = a.row_lse + lh * a.b.total_q + ri.q0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 32 * qh + 8 * (e >> 2) + 4 * hi + (e & 3);
+      const float v = lrow[r < ri.rows ? r : 0];
+      lse2[e] = r < ri.rows ? v * kLog2e : INFINITY;
     }
-    const int64_t room = a.capacity - base;
-    nkept = a.values ? (int)(room < 0 ? 0 : (room < n ? room : n)) : 0;
+  }
+
+  // kept column blocks of the row, ascending, and their col_idx entries:
+  // wave 0, one keep-bit word per lane (a row has at most 64 words), an
+  // exclusive prefix of the words' counts places each lane's columns
+  if (w == 0) {
+    const uint32_t bw = lane < a.words ? a.keep_bits[row * (size_t)a.words + lane] : 0u;
+    const int cnt = __popc(bw);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    uint32_t bits = bw;
+    while (bits) {
+      const int j = lane * 32 + __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (base + pos < a.capacity) a.col_idx[base + pos] = j;
+      jlist[pos++] = j;
+    }
+    if (lane == 63) {
+      const int64_t room = a.capacity - base;
+      nkept = a.values ? (int)(room < 0 ? 0 : (room < incl ? room : incl)) : 0;
+    }
   }
   __syncthreads();
   const int n = nkept;
@@ -321,26 +353,6 @@ __global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
 #pragma unroll
   for (int t = 0; t < XNST - 1; ++t) issue(t);
 
-  // Q rows 32 qh + L % 32 as A operands; lse2 of the lane's 16 output rows
-  bf16x8 qf[KS];
-  {
-    const int r = 32 * qh + l32;
-    const bf16* src = reinterpret_cast<const bf16*>(a.q) + (size_t)l * a.lsq +
-                      ((size_t)(ri.q0 + (r < ri.rows ? r : 0)) * a.H + h) * D + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
-  }
-  const float c2 = (float)(a.scale * kLog2eD);
-  float lse2[16];
-  {
-    const float* __restrict__ lrow = a.row_lse + lh * a.b.total_q + ri.q0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = 32 * qh + 8 * (e >> 2) + 4 * hi + (e & 3);
-      const float v = lrow[r < ri.rows ? r : 0];
-      lse2[e] = r < ri.rows ? v * kLog2e : INFINITY;
-    }
-  }
   const int diag = ri.ncand - 1;
   bf16* __restrict__ vals = reinterpret_cast<bf16*>(a.values);
 
@@ -382,13 +394,16 @@ __global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
       *reinterpret_cast<uint2*>(ot + key * XPITCH + r0 * 2) = pk;
     }
     __syncthreads();
+    // non-temporal stores: the values are read only by a later kernel, and
+    // streaming them past L2 keeps the K blocks the row-blocks of this head
+    // share resident there
     bf16* dst = vals + (size_t)(base + t) * 64 * 64;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int ch = c * 256 + tid;           // 16-byte chunk: key ch / 8, rows 8 (ch % 8) ..
       const int kk = ch >> 3, part = ch & 7;
-      *reinterpret_cast<uint4*>(dst + kk * 64 + part * 8) =
-          *reinterpret_cast<const uint4*>(ot + kk * XPITCH + part * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + kk * XPITCH + part * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * 64 + part * 8));
     }
   }
 }
@@ -452,7 +467,7 @@ size_t extract_mfma_lds_bytes(int d) { return (size_t)XNST * 64 * d * 2; }
 
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (a.values && extract_fast_path(dt, a.B, a.d)) {
+  if (a.values && a.words <= 64 && extract_fast_path(dt, a.B, a.d)) {
     const size_t lds = extract_mfma_lds_bytes(a.d);
     auto kern = a.d == 128 ? extract_mfma_kernel<128> : extract_mfma_kernel<64>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

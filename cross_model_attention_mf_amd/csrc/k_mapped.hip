@@ -142,6 +142,7 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 // tile) from rows whose 16-byte chunks are XOR-swizzled.
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x4 tr_read(const char* lds_generic, unsigned byte_off) {
   auto p = (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)
@@ -620,7 +621,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     const int hl = (k * 8) / D;
     if (qoff + qq < ri.rows && hl < heads_here) {
       bf16* dst = obase + ((size_t)(ri.q0 + qoff + qq) * a.Hr + 8 * grp) * D + (size_t)k * 8;
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(stage + (size_t)qq * 8 * D + (size_t)k * 8);
+      // non-temporal: O is not read again here, and the kept values and V
+      // rows other workgroups still read stay in L2
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(stage + (size_t)qq * 8 * D + (size_t)k * 8);
+      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(dst));
     }
   }
 }
