@@ -223,10 +223,13 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
 // the four consecutive rows 8 (e / 4) + 4 (L / 32) + 0..3 of register group
 // e / 4, so exp2(s c2 - lse2) of four rows packs into one 8-byte bf16 LDS
 // write of the key-major tile; the workgroup then stores the 8 KB tile with
-// 16-byte vector stores.
+// 16-byte vector stores.  The ring has two slots and, for head dim 128, the
+// tile is written into the slot whose K the block just consumed: about 35 KB
+// of LDS and 128 VGPRs let four workgroups share a CU, and that occupancy
+// hides the K fetches better than a deeper ring.
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int XNST = 3;                 // K ring depth
+constexpr int XNST = 2;                 // K ring depth
 constexpr int XPITCH = 64 * 2 + 16;     // bytes per key row of the output tile (16-byte aligned)
 constexpr int kXMaxCb = (MF_MAX_KEYS + 63) / 64;   // column blocks of the longest sequence
 
@@ -256,7 +259,7 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
+__global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
   constexpr int KS = D / 16;
   constexpr int ROWB = D * 2;
   constexpr int CPR = D / 8;
@@ -267,7 +270,9 @@ __global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
   // the block list are separate objects, so their LDS accesses do not have
   // to wait for copies in flight
   extern __shared__ __align__(16) char ring[];
-  __shared__ __align__(16) char otile[2 * OT];
+  // the output tile goes into the K slot just consumed when it fits
+  constexpr bool TILE_IN_RING = STAGE >= OT;
+  __shared__ __align__(16) char otile[TILE_IN_RING ? 16 : OT];
   __shared__ int jlist[kXMaxCb];
   __shared__ int nkept;
 
@@ -375,7 +380,8 @@ __global__ void __launch_bounds__(256, 2) extract_mfma_kernel(ExtractArgs a) {
     }
     // causal mask (diagonal block only) and rows past the row-block: lse2 = inf
     const bool dg = jlist[t] == diag;
-    char* ot = otile + (t & 1) * OT;
+    char* ot = TILE_IN_RING ? ring + (t % XNST) * STAGE : otile;
+    if (TILE_IN_RING) __syncthreads();       // every wave is done reading K from the slot
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float p[4];
