@@ -230,11 +230,16 @@ mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch, 
   return e ? hip_fail(e, fn) : MF_OK;
 }
 
-mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
-                           const int32_t* col_idx, const void* values, const float* W, const void* v, void* o,
-                           void* stream) {
-  mf::clear_error();
-  const char* fn = "mf_mapped_attn_v";
+}  // extern "C"
+
+namespace {
+
+// Validation of one receiver descriptor and its tensors (MF_OK when the call
+// has work or is an empty no-op; *empty tells which).
+mf_status check_receiver(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
+                         const int32_t* col_idx, const void* values, const float* W, const void* v, void* o,
+                         const char* fn, bool* empty) {
+  *empty = false;
   if (!desc) return fail(MF_ERR_INVALID, "%s: desc is NULL", fn);
   mf_status st = check_common(desc->dtype, desc->num_layers, desc->H_r, desc->H_kv_r, desc->d, desc->B, fn);
   if (st) return st;
@@ -260,9 +265,30 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, 
       return fail(MF_ERR_INVALID, "%s: layer strides smaller than one layer", fn);
   }
   if (desc->csr_capacity < 0) return fail(MF_ERR_INVALID, "%s: csr_capacity < 0", fn);
-  if (desc->num_layers == 0 || batch->info.total_rowblocks == 0) return MF_OK;
+  if (desc->num_layers == 0 || batch->info.total_rowblocks == 0) {
+    *empty = true;
+    return MF_OK;
+  }
   if (!row_ptr || !W || !v || !o || (desc->csr_capacity > 0 && (!col_idx || !values)))
     return fail(MF_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  return MF_OK;
+}
+
+mf::MappedRecv receiver_args(const mf_receiver_desc* desc, const float* W, const void* v, void* o, int group0) {
+  mf::MappedRecv r;
+  memset(&r, 0, sizeof(r));
+  r.W = W; r.v = v; r.o = o;
+  r.lsv = desc->layer_stride_v; r.lso = desc->layer_stride_o;
+  r.block_table = desc->block_table; r.page_size = desc->page_size; r.max_pages = desc->max_pages;
+  r.num_pages = desc->num_pages;
+  r.Hr = desc->H_r; r.Hkv = desc->H_kv_r;
+  r.group0 = group0;
+  return r;
+}
+
+// shared fields from desc, receiver 0 from (desc, W, v, o)
+mf::MappedArgs mapped_args(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
+                           const int32_t* col_idx, const void* values, const float* W, const void* v, void* o) {
   mf::MappedArgs a;
   memset(&a, 0, sizeof(a));
   a.b = batch_args(batch);
@@ -273,9 +299,65 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, 
   a.L = desc->num_layers; a.Ls = desc->sender_layers; a.Hs = desc->H_s; a.Hr = desc->H_r; a.Hkv = desc->H_kv_r;
   a.d = desc->d; a.B = desc->B;
   for (int l = 0; l < desc->num_layers; ++l) a.layer_map[l] = desc->layer_map[l];
+  a.nrecv = 1;
+  a.rx[0] = receiver_args(desc, W, v, o, 0);
+  return a;
+}
+
+bool allow_fast_mapped() {
   const char* pv = getenv("MF_PORTABLE_MAPPED");
-  const bool allow_fast = !(pv && pv[0] == '1');
-  const int e = mf::launch_mapped(a, desc->dtype, stream, allow_fast, device_lds_limit());
+  return !(pv && pv[0] == '1');
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
+                           const int32_t* col_idx, const void* values, const float* W, const void* v, void* o,
+                           void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_mapped_attn_v";
+  bool empty = false;
+  mf_status st = check_receiver(desc, batch, row_ptr, col_idx, values, W, v, o, fn, &empty);
+  if (st || empty) return st;
+  const mf::MappedArgs a = mapped_args(desc, batch, row_ptr, col_idx, values, W, v, o);
+  const int e = mf::launch_mapped(a, desc->dtype, stream, allow_fast_mapped(), device_lds_limit());
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_receivers, const mf_batch* batch,
+                                 const int32_t* row_ptr, const int32_t* col_idx, const void* values,
+                                 const float* const* W, const void* const* v, void* const* o, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_mapped_attn_v_multi";
+  if (!descs || !W || !v || !o) return fail(MF_ERR_INVALID, "%s: a receiver array is NULL", fn);
+  if (n_receivers < 1 || n_receivers > MF_MAX_RECEIVERS)
+    return fail(MF_ERR_INVALID, "%s: n_receivers = %d not in [1, %d]", fn, n_receivers, MF_MAX_RECEIVERS);
+  bool empty = false;
+  for (int k = 0; k < n_receivers; ++k) {
+    mf_status st = check_receiver(descs[k], batch, row_ptr, col_idx, values, W[k], v[k], o[k], fn, &empty);
+    if (st) return st;
+  }
+  const mf_receiver_desc* d0 = descs[0];
+  for (int k = 1; k < n_receivers; ++k) {
+    const mf_receiver_desc* dk = descs[k];
+    bool same = dk->dtype == d0->dtype && dk->num_layers == d0->num_layers && dk->sender_layers == d0->sender_layers &&
+                dk->H_s == d0->H_s && dk->d == d0->d && dk->B == d0->B && dk->csr_capacity == d0->csr_capacity;
+    for (int l = 0; same && l < d0->num_layers; ++l) same = dk->layer_map[l] == d0->layer_map[l];
+    if (!same)
+      return fail(MF_ERR_INVALID, "%s: receiver %d differs from receiver 0 in a shared field "
+                  "(dtype, layers, layer_map, sender layers, H_s, d, B or csr_capacity)", fn, k);
+  }
+  if (empty) return MF_OK;   // no layers or no row-blocks: every receiver is empty alike
+  mf::MappedArgs a = mapped_args(d0, batch, row_ptr, col_idx, values, W[0], v[0], o[0]);
+  int groups = 0;
+  for (int k = 0; k < n_receivers; ++k) {
+    a.rx[k] = receiver_args(descs[k], W[k], v[k], o[k], groups);
+    groups += (descs[k]->H_r + 7) / 8;
+  }
+  a.nrecv = n_receivers;
+  const int e = mf::launch_mapped_multi(a, d0->dtype, stream, allow_fast_mapped(), device_lds_limit());
   return e ? hip_fail(e, fn) : MF_OK;
 }
 

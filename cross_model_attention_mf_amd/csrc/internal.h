@@ -72,11 +72,27 @@ struct ExtractArgs {
   double scale;
 };
 
+// One receiver of the fused step: its head mapping, values, output and value
+// layout, and the first of its groups of 8 receiver heads in a launch that
+// serves several receivers.
+struct MappedRecv {
+  const float* W;
+  const void* v;
+  void* o;
+  int64_t lsv, lso;
+  const int32_t* block_table;
+  int32_t page_size, max_pages;
+  int64_t num_pages;
+  int32_t Hr, Hkv;
+  int32_t group0;
+};
+
 struct MappedArgs {
   BatchArgs b;
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const void* values;
+  // the receiver of a single-receiver launch (portable kernel, and rx[0])
   const float* W;
   const void* v;
   void* o;
@@ -87,6 +103,9 @@ struct MappedArgs {
   int64_t csr_capacity;
   int32_t L, Ls, Hs, Hr, Hkv, d, B;
   int32_t layer_map[MF_MAX_LAYERS];
+  // every receiver of the launch (the MFMA kernel reads these)
+  int32_t nrecv;
+  MappedRecv rx[MF_MAX_RECEIVERS];
 };
 
 // Launchers: return 0 on success, a hipError_t value otherwise.
@@ -99,6 +118,9 @@ int launch_select(const SelectArgs& a, void* stream);
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream);
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);
+// several receivers on one CSR: one launch when the MFMA kernel covers them
+// all, else one launch per receiver
+int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);
 size_t select_lds_bytes(int max_cb);
 
 }  // namespace mf

@@ -296,8 +296,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   float* Wsh = reinterpret_cast<float*>(curcol + 64);   // [8 receiver heads][64 sender heads]
 
   // ---- work item.  A unit is one (row-block part, receiver layer); its head
-  // groups run back to back on one XCD (workgroup b runs on XCD b % 8), so
-  // they share that XCD's L2 for the kept values.  Units are dealt to the
+  // groups (those of every receiver of the launch) run back to back on one
+  // XCD (workgroup b runs on XCD b % 8), so they share that XCD's L2 for the
+  // kept values.  Units are dealt to the
   // XCDs in turn, latest row-blocks first: a row-block's union (and work)
   // grows with its causal range, and the short ones then fill the tail.
   const int nitems = a.b.total_rb * C::QH;
@@ -311,20 +312,25 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     item = nitems - 1 - (int)(u / a.L);
     l = (int)(u % a.L);
   }
+  // the receiver this group belongs to, and the group's index in it
+  int rk = 0;
+  for (int k = 1; k < a.nrecv; ++k) rk = grp >= a.rx[k].group0 ? k : rk;
+  const MappedRecv R = a.rx[rk];
+  grp -= R.group0;
   const int rb = item / C::QH, qoff = (item % C::QH) * C::RQ;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
   const int sl = a.layer_map[l];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hq = wave / C::NQT, qt = wave % C::NQT;
   const int lg = lane >> 4, lr = lane & 15;
-  const bool paged = a.block_table != nullptr;
+  const bool paged = R.block_table != nullptr;
 
   // ---- zero the ring and V rows, load the group's W rows
   for (size_t o = (size_t)tid * 16; o < main_bytes; o += (size_t)C::NW * 64 * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
   for (int t = tid; t < 8 * 64; t += C::NW * 64) {
     const int rl = t >> 6, h = t & 63, r = 8 * grp + rl;
-    Wsh[t] = (h < a.Hs && r < a.Hr) ? a.W[((size_t)l * a.Hr + r) * a.Hs + h] : 0.f;
+    Wsh[t] = (h < a.Hs && r < R.Hr) ? R.W[((size_t)l * R.Hr + r) * a.Hs + h] : 0.f;
   }
 
   // ---- union merge state (wave 0): lane h walks sender head h's sorted list
@@ -361,7 +367,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     if (paged && jm != 0x7FFFFFFF) {
       for (int k0 = 0; k0 < B; k0 += 64) {
         const int key = min(jm * B + k0 + lane, ri.klen - 1);
-        async_copy4(a.block_table + (size_t)ri.seq * a.max_pages + key / a.page_size,
+        async_copy4(R.block_table + (size_t)ri.seq * R.max_pages + key / R.page_size,
                     reinterpret_cast<char*>(out->page + k0));
         ++copies;
       }
@@ -374,7 +380,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   __syncthreads();
 
   const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
-  const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(a.v) + (size_t)l * a.lsv;
+  const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(R.v) + (size_t)l * R.lsv;
 
   // P copies: instruction (wave, i) copies head h = wave + i NW, lane L row
   // e = L / 8 (key 8 si + e of the block), chunk L % 8 from source chunk
@@ -409,9 +415,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
   // V rows of 16-key half hh of the block, staged once per value head ->
   // Vs, row 16 kvl + key
-  const int ratio = a.Hr / a.Hkv;
+  const int ratio = R.Hr / R.Hkv;
   const int kv0 = (8 * grp) / ratio;
-  const int nkv = min(8 * grp + 7, a.Hr - 1) / ratio - kv0 + 1;
+  const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
   auto issue_v = [&](const UnionInfo* ui, int hh, int buf) {
     const int ln = opaque(lane);
     const int ninst = nkv * (16 / C::RPI);
@@ -429,12 +435,12 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       size_t tok;
       if (paged) {
         int64_t page = live ? ui->page[kl] : 0;
-        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-        tok = live ? (size_t)page * a.page_size + key % a.page_size : 0;
+        page = page < 0 ? 0 : (page >= R.num_pages ? R.num_pages - 1 : page);
+        tok = live ? (size_t)page * R.page_size + key % R.page_size : 0;
       } else {
         tok = (size_t)ri.k0 + (live ? key : 0);
       }
-      async_copy16(vbase + (tok * a.Hkv + g) * D + 8 * lc, vdst + (size_t)k * 1024);
+      async_copy16(vbase + (tok * R.Hkv + g) * D + 8 * lc, vdst + (size_t)k * 1024);
     }
     return wave < ninst ? (ninst - 1 - wave) / C::NW + 1 : 0;
   };
@@ -613,14 +619,14 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         stage[((size_t)qq * 8 + 4 * hq + i) * D + 16 * nt + lr] = (bf16)O[i][nt][ii];
       }
   __syncthreads();
-  bf16* __restrict__ obase = reinterpret_cast<bf16*>(a.o) + (size_t)l * a.lso;
-  const int heads_here = min(8, a.Hr - 8 * grp);
+  bf16* __restrict__ obase = reinterpret_cast<bf16*>(R.o) + (size_t)l * R.lso;
+  const int heads_here = min(8, R.Hr - 8 * grp);
   constexpr int CPQ = 8 * D * 2 / 16;                  // 16-byte chunks per query row
   for (int c = tid; c < C::RQ * CPQ; c += C::NW * 64) {
     const int qq = c / CPQ, k = c % CPQ;
     const int hl = (k * 8) / D;
     if (qoff + qq < ri.rows && hl < heads_here) {
-      bf16* dst = obase + ((size_t)(ri.q0 + qoff + qq) * a.Hr + 8 * grp) * D + (size_t)k * 8;
+      bf16* dst = obase + ((size_t)(ri.q0 + qoff + qq) * R.Hr + 8 * grp) * D + (size_t)k * 8;
       // non-temporal: O is not read again here, and the kept values and V
       // rows other workgroups still read stay in L2
       const u32x4 ov = *reinterpret_cast<const u32x4*>(stage + (size_t)qq * 8 * D + (size_t)k * 8);
@@ -636,7 +642,8 @@ int launch_fast_h(const MappedArgs& a, void* stream) {
   auto kern = mapped_mfma_kernel<B, D, HP8, KVC>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;
-  const int ngroups = (a.Hr + 7) / 8;
+  int ngroups = 0;
+  for (int k = 0; k < a.nrecv; ++k) ngroups += (a.rx[k].Hr + 7) / 8;
   const long long nu = (long long)a.b.total_rb * C::QH * a.L;
   const long long per_xcd = (nu + kXcds - 1) / kXcds * ngroups;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::NW * 64), lds, (hipStream_t)stream, a, ngroups);
@@ -660,9 +667,18 @@ int launch_fast_k(const MappedArgs& a, void* stream) {
 
 // V buffers sized for 4 value heads per group when the grouped-query
 // layout allows, else for 8
+static int max_group_value_heads(const MappedArgs& a) {
+  int m = 0;
+  for (int k = 0; k < a.nrecv; ++k) {
+    const int g = group_value_heads(a.rx[k].Hr, a.rx[k].Hkv);
+    m = g > m ? g : m;
+  }
+  return m;
+}
+
 template <int B, int D>
 int launch_fast(const MappedArgs& a, void* stream) {
-  return group_value_heads(a.Hr, a.Hkv) <= 4 ? launch_fast_k<B, D, 4>(a, stream) : launch_fast_k<B, D, 8>(a, stream);
+  return max_group_value_heads(a) <= 4 ? launch_fast_k<B, D, 4>(a, stream) : launch_fast_k<B, D, 8>(a, stream);
 }
 
 template <typename T, int B, int D>
@@ -687,13 +703,13 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 }  // namespace
 
-bool mapped_mfma_covers(int B, int d, int Hs, int Hr, int Hkv, size_t lds_limit) {
-  return mapped_mfma_lds_bytes(B, d, Hs, group_value_heads(Hr, Hkv) <= 4 ? 4 : 8) <= lds_limit;
+bool mapped_mfma_covers(int B, int d, int Hs, int kv_heads_per_group, size_t lds_limit) {
+  return mapped_mfma_lds_bytes(B, d, Hs, kv_heads_per_group <= 4 ? 4 : 8) <= lds_limit;
 }
 
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, a.Hr, a.Hkv, lds_limit)) {
+  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, max_group_value_heads(a), lds_limit)) {
     switch (a.B * 1000 + a.d) {
       case 64064: return launch_fast<64, 64>(a, stream);
       case 64128: return launch_fast<64, 128>(a, stream);
@@ -702,6 +718,27 @@ int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fas
     }
   }
   return dt == MF_BF16 ? launch_gd<bf16>(a, stream) : launch_gd<float>(a, stream);
+}
+
+int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
+  if (a.b.total_rb == 0 || a.L == 0) return 0;
+  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, max_group_value_heads(a), lds_limit) &&
+      (a.B == 64 || a.B == 128) && (a.d == 64 || a.d == 128))
+    return launch_mapped(a, dt, stream, allow_fast, lds_limit);
+  // one launch per receiver
+  for (int k = 0; k < a.nrecv; ++k) {
+    MappedArgs one = a;
+    const MappedRecv& r = a.rx[k];
+    one.W = r.W; one.v = r.v; one.o = r.o; one.lsv = r.lsv; one.lso = r.lso;
+    one.block_table = r.block_table; one.page_size = r.page_size; one.max_pages = r.max_pages;
+    one.num_pages = r.num_pages; one.Hr = r.Hr; one.Hkv = r.Hkv;
+    one.nrecv = 1;
+    one.rx[0] = r;
+    one.rx[0].group0 = 0;
+    const int e = launch_mapped(one, dt, stream, allow_fast, lds_limit);
+    if (e) return e;
+  }
+  return 0;
 }
 
 }  // namespace mf

@@ -20,9 +20,11 @@ MF_OK, MF_ERR_INVALID, MF_ERR_UNSUPPORTED, MF_ERR_CAPACITY, MF_ERR_HIP, MF_ERR_W
 MF_F32, MF_BF16 = 0, 1
 MF_MAX_KEYS = 40448
 MF_MAX_LAYERS = 256
+MF_MAX_RECEIVERS = 4
 EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_compress_workspace_size", "mf_compress_blocks",
-           "mf_mapped_attn_v", "mf_status_string", "mf_last_error_message", "mf_version")
+           "mf_mapped_attn_v", "mf_mapped_attn_v_multi", "mf_status_string", "mf_last_error_message",
+           "mf_version")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -92,7 +94,10 @@ def lib():
                                      ctypes.c_float, vp, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
     L.mf_mapped_attn_v.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
                                    vp, vp, vp]
-    for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v"):
+    L.mf_mapped_attn_v_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(ReceiverDesc)), ctypes.c_int,
+                                         ctypes.POINTER(BatchC), vp, vp, vp, ctypes.POINTER(vp),
+                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v", "mf_mapped_attn_v_multi"):
         getattr(L, f).restype = ctypes.c_int
     L.mf_status_string.argtypes = [ctypes.c_int]
     L.mf_status_string.restype = ctypes.c_char_p
@@ -230,3 +235,16 @@ def mapped_attn_v(desc: ReceiverDesc, batch: Batch, row_ptr, col_idx, values, W,
     _check(lib().mf_mapped_attn_v(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(row_ptr),
                                   _ptr(col_idx), _ptr(values), _ptr(W), _ptr(v), _ptr(o),
                                   _stream(stream)))
+
+
+def mapped_attn_v_multi(descs: Sequence[ReceiverDesc], batch: Batch, row_ptr, col_idx, values,
+                        Ws, vs, os_, stream=None):
+    """Several receivers of one CSR in one call: descs[k], Ws[k], vs[k], os_[k] as in
+    mapped_attn_v."""
+    n = len(descs)
+    dp = (ctypes.POINTER(ReceiverDesc) * n)(*[ctypes.pointer(d) for d in descs])
+    wp = (ctypes.c_void_p * n)(*[_ptr(w) for w in Ws])
+    vp_ = (ctypes.c_void_p * n)(*[_ptr(x) for x in vs])
+    op = (ctypes.c_void_p * n)(*[_ptr(x) for x in os_])
+    _check(lib().mf_mapped_attn_v_multi(dp, n, ctypes.byref(batch.c), _ptr(row_ptr), _ptr(col_idx),
+                                        _ptr(values), wp, vp_, op, _stream(stream)))

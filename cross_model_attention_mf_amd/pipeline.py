@@ -91,3 +91,26 @@ def mapped(st: SenderState, W: torch.Tensor, v: torch.Tensor, layer_map: Sequenc
                             st.col_idx.numel(), block_table, page_size)
     mf.mapped_attn_v(desc, st.batch, st.row_ptr, st.col_idx, st.values, W, v, out, stream)
     return out
+
+
+def mapped_multi(st: SenderState, receivers: Sequence[tuple], layer_map: Sequence[int], stream=None):
+    """Several receivers of one sender state in one call.  receivers: (W, v) or
+    (W, v, block_table, page_size) per receiver, shaped as for `mapped`.
+    Returns the list of O tensors."""
+    descs, Ws, vs, outs = [], [], [], []
+    for rcv in receivers:
+        W, v = rcv[0], rcv[1]
+        block_table = rcv[2] if len(rcv) > 2 else None
+        page_size = rcv[3] if len(rcv) > 3 else 0
+        if W.dim() == 2:
+            W = W[None]
+        if v.dim() == (4 if block_table is not None else 3):
+            v = v[None]
+        L_r, H_r, H_s = W.shape
+        d = v.shape[-1]
+        out = torch.empty((L_r, st.batch.info.total_q, H_r, d), dtype=v.dtype, device=v.device)
+        descs.append(mf.receiver_desc(v, H_s, H_r, d, st.B, layer_map, st.desc.num_layers, out[0].numel(),
+                                      st.col_idx.numel(), block_table, page_size))
+        Ws.append(W); vs.append(v); outs.append(out)
+    mf.mapped_attn_v_multi(descs, st.batch, st.row_ptr, st.col_idx, st.values, Ws, vs, outs, stream)
+    return outs

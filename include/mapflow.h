@@ -226,6 +226,28 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch,
                            const void* values, const float* W, const void* v,
                            void* o, void* stream);
 
+#define MF_MAX_RECEIVERS 4
+
+/* Several receivers reuse one sender state in one launch (one sender state
+ * serving several downstream models, section "让复用真正省时…", paragraph
+ * "第二").  Receiver k is described by descs[k], W[k], v[k] and o[k] exactly as
+ * in mf_mapped_attn_v, and gets the same output.  All descriptors must share
+ * dtype, num_layers, the layer_map contents, sender_layers, H_s, d, B and
+ * csr_capacity; each has its own H_r, H_kv_r, value layout (packed or paged)
+ * and strides.  The head groups of every receiver for one row-block and
+ * layer run back to back on one XCD, so the kept values they all read are
+ * fetched from HBM about once instead of once per receiver.
+ *   descs, W, v, o  HOST arrays of n_receivers (1 <= n <= MF_MAX_RECEIVERS)
+ *                   pointers; the tensors they point to are DEVICE
+ *   o[k] must not overlap another receiver's o or any input.
+ * Errors: MF_ERR_INVALID for a NULL array or a descriptor that differs in a
+ * shared field, plus everything mf_mapped_attn_v reports per receiver. */
+mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_receivers,
+                                 const mf_batch* batch, const int32_t* row_ptr,
+                                 const int32_t* col_idx, const void* values,
+                                 const float* const* W, const void* const* v,
+                                 void* const* o, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */
 /* ------------------------------------------------------------------------ */

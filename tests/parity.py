@@ -52,7 +52,10 @@ class GpuRun:
 
 
 def run_gpu(wl: synth.Workload, tau: float, layers: Sequence[int], step: int = 0,
-            layer_map: Optional[Sequence[int]] = None, streams: bool = False) -> GpuRun:
+            layer_map: Optional[Sequence[int]] = None, streams: bool = False,
+            multi: bool = False) -> GpuRun:
+    """streams: one launch per receiver, each on its own stream; multi: every
+    receiver in one mf_mapped_attn_v_multi call."""
     lay = synth.batch_layout(wl, step)
     inputs = [synth.layer_inputs(wl, l, step, lay) for l in layers]
     dev = torch.device("cuda")
@@ -82,7 +85,9 @@ def run_gpu(wl: synth.Workload, tau: float, layers: Sequence[int], step: int = 0
             launches.append((W, pool, bt))
         else:
             launches.append((W, torch.stack(vs).to(dev), None))
-    if streams and len(launches) > 1:
+    if multi:
+        outs = pipeline.mapped_multi(st, [(W, v, bt, wl.page_size) for W, v, bt in launches], lm)
+    elif streams and len(launches) > 1:
         ss = [torch.cuda.Stream() for _ in launches]
         cur = torch.cuda.current_stream()
         for s in ss:

@@ -187,6 +187,45 @@ def test_mapped_validation(layer_map, kw, status):
     assert st == status, mf.lib().mf_last_error_message()
 
 
+def _multi(descs, ptrs=16):
+    n = len(descs)
+    dp = (ctypes.POINTER(mf.ReceiverDesc) * max(n, 1))(*[ctypes.pointer(d) for d in descs])
+    arr = (ctypes.c_void_p * max(n, 1))(*([ptrs] * max(n, 1)))
+    return dp, arr
+
+
+@pytest.mark.parametrize("case", ["null", "zero", "too_many", "shared_field", "layer_map", "per_receiver"])
+def test_mapped_multi_validation(case):
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    r0 = _receiver([0, 1])
+    descs = [r0, _receiver([0, 1], H_r=8, H_kv_r=2)]
+    n = len(descs)
+    if case == "shared_field":
+        descs[1] = _receiver([0, 1], H_s=5)
+    elif case == "layer_map":
+        descs[1] = _receiver([1, 0])
+    elif case == "per_receiver":
+        descs[1] = _receiver([0, 1], H_kv_r=5)            # kv heads do not divide H_r
+    elif case == "too_many":
+        descs = [r0] * (mf.MF_MAX_RECEIVERS + 1)
+        n = len(descs)
+    elif case == "zero":
+        n = 0
+    dp, arr = _multi(descs)
+    if case == "null":
+        st = mf.lib().mf_mapped_attn_v_multi(dp, n, ctypes.byref(b), 16, 16, 16, None, arr, arr, None)
+    else:
+        st = mf.lib().mf_mapped_attn_v_multi(dp, n, ctypes.byref(b), 16, 16, 16, arr, arr, arr, None)
+    assert st == mf.MF_ERR_INVALID, mf.lib().mf_last_error_message()
+
+
+def test_mapped_multi_empty_batch_is_a_noop():
+    b = _host_batch([0, 0], [0, 0], None, 64)
+    descs = [_receiver([0]), _receiver([0], H_r=8, H_kv_r=8)]
+    dp, arr = _multi(descs, ptrs=None)
+    assert mf.lib().mf_mapped_attn_v_multi(dp, 2, ctypes.byref(b), None, None, None, arr, arr, arr, None) == mf.MF_OK
+
+
 def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mf, "_lib", None)
     monkeypatch.setattr(mf, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -109,6 +109,33 @@ def test_32k_one_sender_two_receivers_two_streams():
         assert torch.equal(a, b)
 
 
+def test_several_receivers_in_one_launch():
+    # one sender (40 heads, B = 128) feeding receivers of 32 and 24 heads in one
+    # call: oracle parity, and the same outputs as one launch per receiver
+    wl = W5.replace(seqlens=(4096,))
+    multi = parity.run_gpu(wl, wl.tau, [0], multi=True)
+    n = multi.state.batch.total_rowblocks
+    parity.check_layer(multi, 0, rowblocks=[0, n // 2, n - 1])
+    sep = parity.run_gpu(wl, wl.tau, [0])
+    for a, b in zip(multi.outs, sep.outs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (32, 64)])
+def test_several_receivers_varlen_paged_gqa(B, d):
+    # grouped-query first receiver (6 heads over 3 value heads) and a 9-head
+    # second one, paged values, varlen chunked batch, two layers
+    wl = tiny_structured("bf16", workload_id=16, B=B, d=d, H_s=12, H_r=6, H_kv_r=3,
+                         extra_receivers=((9, 0.5),), paged=True, page_size=16,
+                         seqlens=(3 * B + 17, B + 5, 2 * B), chunk=2 * B, num_layers=2)
+    multi = parity.run_gpu(wl, 0.9, [0, 1], step=1, multi=True)
+    for li in range(2):
+        parity.check_layer(multi, li)
+    sep = parity.run_gpu(wl, 0.9, [0, 1], step=1)
+    for a, b in zip(multi.outs, sep.outs):
+        assert torch.equal(a, b)
+
+
 def test_capacity_sync_and_async():
     wl = tiny_structured("bf16", seqlens=(512,))
     run = parity.run_gpu(wl, 0.8, [0])
