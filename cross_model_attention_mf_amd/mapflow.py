@@ -23,7 +23,9 @@ MF_MAX_LAYERS = 256
 MF_MAX_RECEIVERS = 4
 EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_compress_workspace_size", "mf_compress_blocks",
-           "mf_mapped_attn_v", "mf_mapped_attn_v_multi", "mf_status_string", "mf_last_error_message",
+           "mf_mapped_attn_v", "mf_mapped_attn_v_multi", "mf_prefix_block_hashes", "mf_map_cache_create",
+           "mf_map_cache_destroy", "mf_map_cache_insert", "mf_map_cache_lookup", "mf_map_cache_release",
+           "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_status_string", "mf_last_error_message",
            "mf_version")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -58,6 +60,18 @@ class ReceiverDesc(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int64),
                 ("csr_capacity", ctypes.c_int64)]
+
+
+class MapCacheDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("num_layers", ctypes.c_int32), ("H_s", ctypes.c_int32),
+                ("B", ctypes.c_int32)]
+
+
+class MapCacheStats(ctypes.Structure):
+    _fields_ = [("entries", ctypes.c_int64), ("pinned_entries", ctypes.c_int64),
+                ("bytes_used", ctypes.c_int64), ("bytes_capacity", ctypes.c_int64),
+                ("blocks_hit", ctypes.c_int64), ("blocks_missed", ctypes.c_int64),
+                ("evictions", ctypes.c_int64)]
 
 
 class MapflowError(RuntimeError):
@@ -97,7 +111,22 @@ def lib():
     L.mf_mapped_attn_v_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(ReceiverDesc)), ctypes.c_int,
                                          ctypes.POINTER(BatchC), vp, vp, vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
-    for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v", "mf_mapped_attn_v_multi"):
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    L.mf_prefix_block_hashes.argtypes = [_i32p, i64, i32, ctypes.c_uint64, u64p]
+    L.mf_prefix_block_hashes.restype = i64
+    L.mf_map_cache_create.argtypes = [ctypes.POINTER(MapCacheDesc), vp, sz, ctypes.POINTER(vp)]
+    L.mf_map_cache_destroy.argtypes = [vp]
+    L.mf_map_cache_destroy.restype = None
+    L.mf_map_cache_insert.argtypes = [vp, u64p, i32, _i32p, i32, i32, vp, vp, vp]
+    L.mf_map_cache_lookup.argtypes = [vp, u64p, i32]
+    L.mf_map_cache_lookup.restype = i32
+    L.mf_map_cache_release.argtypes = [vp, u64p, i32]
+    L.mf_map_cache_release.restype = None
+    L.mf_map_cache_splice.argtypes = [vp, u64p, i32, i32, _i32p, i32, i32, vp, vp, vp, vp, vp, i64,
+                                      ctypes.POINTER(i64), vp]
+    L.mf_map_cache_get_stats.argtypes = [vp, ctypes.POINTER(MapCacheStats)]
+    for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v", "mf_mapped_attn_v_multi",
+              "mf_map_cache_create", "mf_map_cache_insert", "mf_map_cache_splice", "mf_map_cache_get_stats"):
         getattr(L, f).restype = ctypes.c_int
     L.mf_status_string.argtypes = [ctypes.c_int]
     L.mf_status_string.restype = ctypes.c_char_p
@@ -248,3 +277,71 @@ def mapped_attn_v_multi(descs: Sequence[ReceiverDesc], batch: Batch, row_ptr, co
     op = (ctypes.c_void_p * n)(*[_ptr(x) for x in os_])
     _check(lib().mf_mapped_attn_v_multi(dp, n, ctypes.byref(batch.c), _ptr(row_ptr), _ptr(col_idx),
                                         _ptr(values), wp, vp_, op, _stream(stream)))
+
+
+def prefix_block_hashes(tokens, B: int, parent: int = 0) -> np.ndarray:
+    """Chained block keys of a token sequence (one per full block of B)."""
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    out = np.zeros(max(len(t) // B, 1), dtype=np.uint64)
+    n = lib().mf_prefix_block_hashes(t.ctypes.data_as(_i32p), len(t), int(B), int(parent),
+                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)))
+    if n < 0:
+        raise MapflowError(MF_ERR_INVALID, "mf_prefix_block_hashes: bad arguments")
+    return out[:n]
+
+
+class MapCache:
+    """Prefix cache of compressed maps in a device pool (a uint8 CUDA tensor the
+    object keeps alive)."""
+
+    def __init__(self, dtype: torch.dtype, num_layers: int, H_s: int, B: int, pool_bytes: int,
+                 device=None):
+        self.pool = torch.empty(pool_bytes, dtype=torch.uint8, device=device or "cuda")
+        self.desc = MapCacheDesc(dtype_code(dtype), num_layers, H_s, B)
+        h = ctypes.c_void_p()
+        _check(lib().mf_map_cache_create(ctypes.byref(self.desc), _ptr(self.pool), pool_bytes, ctypes.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().mf_map_cache_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+    @staticmethod
+    def _u64(keys):
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        return k, k.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+
+    def insert(self, keys, row_ptr_host: np.ndarray, total_rb: int, rb_first: int, col_idx, values, stream=None):
+        k, kp = self._u64(keys)
+        rp = np.ascontiguousarray(np.asarray(row_ptr_host, dtype=np.int32))
+        _check(lib().mf_map_cache_insert(self.h, kp, len(k), rp.ctypes.data_as(_i32p), int(total_rb), int(rb_first),
+                                         _ptr(col_idx), _ptr(values), _stream(stream)))
+
+    def lookup(self, keys) -> int:
+        k, kp = self._u64(keys)
+        return int(lib().mf_map_cache_lookup(self.h, kp, len(k)))
+
+    def release(self, keys, m: int):
+        k, kp = self._u64(keys)
+        lib().mf_map_cache_release(self.h, kp, int(m))
+
+    def splice(self, keys, m: int, n_blocks: int, suffix_row_ptr_host, suffix_total_rb: int, suffix_rb_first: int,
+               suffix_col_idx, suffix_values, row_ptr_out, col_idx_out, values_out, stream=None) -> int:
+        k, kp = self._u64(keys if len(keys) else [0])
+        rp = np.ascontiguousarray(np.asarray(suffix_row_ptr_host if suffix_row_ptr_host is not None else [0],
+                                             dtype=np.int32))
+        nnz = ctypes.c_int64(-1)
+        cap = col_idx_out.numel() if col_idx_out is not None else 0
+        _check(lib().mf_map_cache_splice(self.h, kp, int(m), int(n_blocks), rp.ctypes.data_as(_i32p),
+                                         int(suffix_total_rb), int(suffix_rb_first), _ptr(suffix_col_idx),
+                                         _ptr(suffix_values), _ptr(row_ptr_out), _ptr(col_idx_out),
+                                         _ptr(values_out), cap, ctypes.byref(nnz), _stream(stream)))
+        return int(nnz.value)
+
+    def stats(self) -> dict:
+        st = MapCacheStats()
+        _check(lib().mf_map_cache_get_stats(self.h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in MapCacheStats._fields_}

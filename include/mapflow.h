@@ -249,6 +249,90 @@ mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_rec
                                  void* const* o, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Prefix cache of compressed maps                                          */
+/* ------------------------------------------------------------------------ */
+/* Requests that share a token prefix share the sender's compressed rows for
+ * it (a cache managed by shared prefix, section "让复用真正省时…", paragraph
+ * "第二").  In a causal sender, row-block i of a sequence depends only on
+ * tokens [0, (i+1) B), so its CSR rows (every layer and sender head) are keyed
+ * by a chained hash of the first i + 1 blocks of tokens.
+ *
+ * Row numbering used below: in a CSR written by mf_compress_blocks for a batch
+ * of R row-blocks, the row of (layer l, sender head h, row-block r) is
+ * (l * H_s + h) * R + r. */
+
+/* FNV-1a 64-bit (offset basis 0xcbf29ce484222325, prime 0x100000001b3),
+ * chained over blocks: hash[i] is FNV-1a over the 8 bytes of hash[i - 1]
+ * (little-endian; `parent` for i = 0, 0 at a sequence start) followed by the
+ * B tokens of block i (int32 little-endian).  tokens and hashes_out are HOST
+ * arrays; one hash per full block (n_tokens / B) is written.  Returns that
+ * count, or -1 for a NULL pointer, n_tokens < 0 or B < 1. */
+int64_t mf_prefix_block_hashes(const int32_t* tokens, int64_t n_tokens, int32_t B,
+                               uint64_t parent, uint64_t* hashes_out);
+
+typedef struct mf_map_cache mf_map_cache;
+
+typedef struct {
+  mf_dtype dtype;             /* of the block values */
+  int32_t num_layers;         /* CSR layers an entry holds */
+  int32_t H_s;                /* sender heads */
+  int32_t B;
+} mf_map_cache_desc;
+
+typedef struct {
+  int64_t entries, pinned_entries;
+  int64_t bytes_used, bytes_capacity;   /* of the device pool */
+  int64_t blocks_hit, blocks_missed;    /* by mf_map_cache_lookup */
+  int64_t evictions;
+} mf_map_cache_stats;
+
+/* An entry holds the CSR rows of row-blocks [0, n) of one sequence for every
+ * layer and head, in `pool` (DEVICE, pool_bytes, owned by the caller; it must
+ * outlive the cache).  The index stays on the host.  Entries not pinned by a
+ * lookup are evicted least recently used first when an insert needs room.
+ * One caller at a time, and every call on one stream (or synchronised
+ * between streams): the cache reuses a small table area in the pool. */
+mf_status mf_map_cache_create(const mf_map_cache_desc* desc, void* pool, size_t pool_bytes,
+                              mf_map_cache** out);
+void mf_map_cache_destroy(mf_map_cache* cache);
+
+/* Copies the CSR rows of the first n_blocks row-blocks of one sequence into a
+ * new entry keyed by hashes[0..n_blocks) (HOST).  The sequence's rows must
+ * start at token 0 and occupy rows rb_first .. rb_first + n_blocks - 1 of a
+ * CSR with total_rb row-blocks per (layer, head); row_ptr_host is a HOST copy
+ * of that CSR's row_ptr, col_idx and values are DEVICE.  Nothing is copied
+ * when hashes[n_blocks - 1] is already cached.  MF_ERR_CAPACITY when the pool
+ * cannot hold the entry even after evicting every unpinned entry. */
+mf_status mf_map_cache_insert(mf_map_cache* cache, const uint64_t* hashes, int32_t n_blocks,
+                              const int32_t* row_ptr_host, int32_t total_rb, int32_t rb_first,
+                              const int32_t* col_idx, const void* values, void* stream);
+
+/* Number m of leading hashes[0..n) (HOST) the cache holds.  A nonzero m pins
+ * the entry holding them until mf_map_cache_release(cache, hashes, m). */
+int32_t mf_map_cache_lookup(mf_map_cache* cache, const uint64_t* hashes, int32_t n);
+void mf_map_cache_release(mf_map_cache* cache, const uint64_t* hashes, int32_t m);
+
+/* Writes the CSR mf_compress_blocks would write for one sequence of n_blocks
+ * row-blocks (a single-sequence batch from token 0): row-blocks [0, m) from
+ * the pinned entry of hashes[0..m), row-blocks [m, n_blocks) from a CSR of
+ * the same sequence compressed as a chunk that starts at row m * B.  That
+ * suffix CSR has suffix_total_rb row-blocks per (layer, head), the sequence
+ * at rows suffix_rb_first .. + n_blocks - m - 1; suffix_row_ptr_host is HOST,
+ * its col_idx and values DEVICE.  Outputs are DEVICE: row_ptr_out
+ * [num_layers * H_s * n_blocks + 1], col_idx_out and values_out with room for
+ * capacity_blocks entries; *nnz_out (HOST) receives the entry count.
+ * MF_ERR_CAPACITY when it exceeds capacity_blocks (nothing is written then);
+ * MF_ERR_INVALID when hashes[0..m) are not all held by one pinned entry. */
+mf_status mf_map_cache_splice(mf_map_cache* cache, const uint64_t* hashes, int32_t m,
+                              int32_t n_blocks, const int32_t* suffix_row_ptr_host,
+                              int32_t suffix_total_rb, int32_t suffix_rb_first,
+                              const int32_t* suffix_col_idx, const void* suffix_values,
+                              int32_t* row_ptr_out, int32_t* col_idx_out, void* values_out,
+                              int64_t capacity_blocks, int64_t* nnz_out, void* stream);
+
+mf_status mf_map_cache_get_stats(const mf_map_cache* cache, mf_map_cache_stats* out);
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostics                                                              */
 /* ------------------------------------------------------------------------ */
 

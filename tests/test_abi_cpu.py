@@ -41,6 +41,8 @@ def _c_layout(tmp_path):
         "mf_batch": [f for f, _ in mf.BatchC._fields_],
         "mf_sender_desc": [f for f, _ in mf.SenderDesc._fields_],
         "mf_receiver_desc": [f for f, _ in mf.ReceiverDesc._fields_],
+        "mf_map_cache_desc": [f for f, _ in mf.MapCacheDesc._fields_],
+        "mf_map_cache_stats": [f for f, _ in mf.MapCacheStats._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mapflow.h"', 'int main(void) {']
     for st, fs in fields.items():
@@ -59,7 +61,8 @@ def _c_layout(tmp_path):
 def test_struct_layouts_match_header(tmp_path):
     c = _c_layout(tmp_path)
     for name, cls in [("mf_plan_info", mf.PlanInfo), ("mf_batch", mf.BatchC),
-                      ("mf_sender_desc", mf.SenderDesc), ("mf_receiver_desc", mf.ReceiverDesc)]:
+                      ("mf_sender_desc", mf.SenderDesc), ("mf_receiver_desc", mf.ReceiverDesc),
+                      ("mf_map_cache_desc", mf.MapCacheDesc), ("mf_map_cache_stats", mf.MapCacheStats)]:
         assert c[(name, "sizeof")] == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert c[(name, f)] == getattr(cls, f).offset, (name, f)
@@ -231,3 +234,53 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mf, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         mf.lib()
+
+
+# ---- prefix cache of compressed maps: host-side behaviour (no device work)
+
+def test_prefix_block_hashes_match_oracle_chain():
+    from oracle import prefix_hash_oracle as ph
+    rng = np.random.default_rng(7)
+    toks = rng.integers(-2**31, 2**31, size=1000, dtype=np.int64).astype(np.int32)
+    for B, parent in [(64, 0), (32, 0x0123456789ABCDEF), (7, 5)]:
+        got = mf.prefix_block_hashes(toks, B, parent)
+        want = ph.prefix_block_keys(toks.tolist(), B, parent)
+        assert len(got) == len(toks) // B
+        assert [int(x) for x in got] == want
+    # keys chain: a continuation from the last key of a prefix equals the tail
+    # of the whole sequence's keys
+    full = mf.prefix_block_hashes(toks[:640], 64)
+    tail = mf.prefix_block_hashes(toks[320:640], 64, int(full[4]))
+    assert list(tail) == list(full[5:])
+    assert len(mf.prefix_block_hashes(toks[:63], 64)) == 0
+    assert mf.lib().mf_prefix_block_hashes(None, 10, 64, 0, None) == -1
+
+
+def test_map_cache_host_paths():
+    # a fake 256-byte aligned "device" address: create, lookup and release
+    # touch only the host index
+    d = mf.MapCacheDesc(mf.MF_BF16, 2, 4, 64)
+    h = ctypes.c_void_p()
+    L = mf.lib()
+    assert L.mf_map_cache_create(ctypes.byref(d), 1 << 20, 1 << 20, ctypes.byref(h)) == mf.MF_OK
+    try:
+        keys = (ctypes.c_uint64 * 3)(1, 2, 3)
+        assert L.mf_map_cache_lookup(h, keys, 3) == 0
+        L.mf_map_cache_release(h, keys, 0)
+        st = mf.MapCacheStats()
+        assert L.mf_map_cache_get_stats(h, ctypes.byref(st)) == mf.MF_OK
+        assert st.blocks_missed == 3 and st.entries == 0 and st.bytes_capacity > 0
+        # splice with nothing cached refuses a cached prefix it does not hold
+        nnz = ctypes.c_int64()
+        rp = (ctypes.c_int32 * 2)(0, 0)
+        assert L.mf_map_cache_splice(h, keys, 1, 2, rp, 1, 0, None, None, 16, None, None, 0,
+                                     ctypes.byref(nnz), None) == mf.MF_ERR_INVALID
+        # insert argument checks come before any copy
+        assert L.mf_map_cache_insert(h, keys, 0, rp, 1, 0, None, None, None) == mf.MF_ERR_INVALID
+        assert L.mf_map_cache_insert(h, keys, 2, rp, 1, 0, None, None, None) == mf.MF_ERR_INVALID
+    finally:
+        L.mf_map_cache_destroy(h)
+    bad = mf.MapCacheDesc(mf.MF_BF16, 0, 4, 64)
+    assert L.mf_map_cache_create(ctypes.byref(bad), 1 << 20, 1 << 20, ctypes.byref(h)) == mf.MF_ERR_INVALID
+    assert L.mf_map_cache_create(ctypes.byref(d), (1 << 20) + 16, 1 << 20, ctypes.byref(h)) == mf.MF_ERR_INVALID
+    assert L.mf_map_cache_create(ctypes.byref(d), 1 << 20, 512, ctypes.byref(h)) == mf.MF_ERR_CAPACITY

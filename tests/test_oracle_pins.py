@@ -422,3 +422,31 @@ def test_planted_renormalised_values(monkeypatch):
     _with(monkeypatch, "extract_blocks", bad)
     with pytest.raises(AssertionError):
         test_values_equal_dense_entries()
+
+
+# ---- block keys of the prefix cache (FNV-1a 64, chained per block)
+
+def test_fnv1a_64_published_vectors():
+    # test vectors published with the FNV reference description
+    from oracle import prefix_hash_oracle as ph
+    assert ph.fnv1a_64(b"") == 0xCBF29CE484222325
+    assert ph.fnv1a_64(b"a") == 0xAF63DC4C8601EC8C
+    assert ph.fnv1a_64(b"foobar") == 0x85944171F73967E8
+
+
+def test_prefix_block_keys_depend_on_the_prefix_only():
+    from oracle import prefix_hash_oracle as ph
+    rng = np.random.default_rng(3)
+    toks = rng.integers(0, 50000, size=8 * 16).tolist()
+    keys = ph.prefix_block_keys(toks, 16)
+    assert len(keys) == 8 and len(set(keys)) == 8
+    # a token changed in block 5 changes keys 5.. and no earlier one
+    t2 = list(toks)
+    t2[5 * 16 + 3] += 1
+    k2 = ph.prefix_block_keys(t2, 16)
+    assert k2[:5] == keys[:5] and all(a != b for a, b in zip(k2[5:], keys[5:]))
+    # the first key is FNV-1a of eight zero bytes and the block's tokens
+    data = (0).to_bytes(8, "little") + b"".join(int(t).to_bytes(4, "little") for t in toks[:16])
+    assert keys[0] == ph.fnv1a_64(data)
+    # a trailing partial block gets no key
+    assert len(ph.prefix_block_keys(toks[:16 * 3 + 5], 16)) == 3
