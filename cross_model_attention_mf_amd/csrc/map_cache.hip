@@ -37,23 +37,56 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Segment {
   uint64_t src, dst, bytes;
+  uint64_t first;  // index of the segment's first chunk in the launch
 };
 
-// one workgroup per segment; 16-byte copies when source, destination and
-// length allow, else 4-byte (col_idx ranges), else bytes
-__global__ void __launch_bounds__(256) gather_segments(const Segment* __restrict__ segs) {
-  const Segment sg = segs[blockIdx.x];
-  const char* src = reinterpret_cast<const char*>(sg.src);
-  char* dst = reinterpret_cast<char*>(sg.dst);
-  const uint64_t n = sg.bytes;
-  if (((sg.src | sg.dst | n) & 15) == 0) {
-    for (uint64_t o = (uint64_t)threadIdx.x * 16; o < n; o += 256 * 16)
-      *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
-  } else if (((sg.src | sg.dst | n) & 3) == 0) {
-    for (uint64_t o = (uint64_t)threadIdx.x * 4; o < n; o += 256 * 4)
+constexpr uint64_t kChunk = 64 * 1024;  // bytes per workgroup
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One workgroup per 64 KB chunk of the segment list, so a few long value
+// ranges still spread over the whole chip.  The chunk's segment is found by
+// a binary search over the segments' first-chunk indices (uniform across the
+// workgroup).  16-byte copies when source, destination and length allow,
+// else 4-byte (col_idx ranges), else bytes; each thread issues its loads
+// before its stores.
+__global__ void __launch_bounds__(kGatherThreads) gather_segments(const Segment* __restrict__ segs, int nseg) {
+  const uint64_t g = blockIdx.x;
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].first <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  const Segment sg = segs[lo];
+  const uint64_t off = (g - sg.first) * kChunk;
+  if (off >= sg.bytes) return;
+  const uint64_t n = sg.bytes - off < kChunk ? sg.bytes - off : kChunk;
+  const char* __restrict__ src = reinterpret_cast<const char*>(sg.src) + off;
+  char* __restrict__ dst = reinterpret_cast<char*>(sg.dst) + off;
+  const int tid = threadIdx.x;
+  if (((sg.src | sg.dst | sg.bytes) & 15) == 0) {
+    constexpr uint64_t kStep = (uint64_t)kGatherThreads * 16 * kGatherUnroll;
+    for (uint64_t base = 0; base < n; base += kStep) {
+      u32x4 r[kGatherUnroll];
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const uint64_t o = base + ((uint64_t)u * kGatherThreads + tid) * 16;
+        if (o < n) r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + o));
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        const uint64_t o = base + ((uint64_t)u * kGatherThreads + tid) * 16;
+        if (o < n) __builtin_nontemporal_store(r[u], reinterpret_cast<u32x4*>(dst + o));
+      }
+    }
+  } else if (((sg.src | sg.dst | sg.bytes) & 3) == 0) {
+    for (uint64_t o = (uint64_t)tid * 4; o < n; o += kGatherThreads * 4)
       *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
   } else {
-    for (uint64_t o = threadIdx.x; o < n; o += 256) dst[o] = src[o];
+    for (uint64_t o = tid; o < n; o += kGatherThreads) dst[o] = src[o];
   }
 }
 
@@ -155,11 +188,19 @@ struct mf_map_cache {
     if (segs.empty()) return MF_OK;
     const size_t bytes = segs.size() * sizeof(Segment);
     if (bytes > table_bytes) return fail(MF_ERR_UNSUPPORTED, "%s: %zu copy segments exceed the table", fn, segs.size());
+    uint64_t chunks = 0;
+    for (Segment& sg : segs) {
+      sg.first = chunks;
+      chunks += (sg.bytes + kChunk - 1) / kChunk;
+    }
+    if (chunks == 0) return MF_OK;
+    if (chunks > 0x7fffffffull) return fail(MF_ERR_UNSUPPORTED, "%s: %llu bytes to copy in one call", fn,
+                                            (unsigned long long)(chunks * kChunk));
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(pool, segs.data(), bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(gather_segments, dim3((unsigned)segs.size()), dim3(256), 0, s,
-                         reinterpret_cast<const Segment*>(pool));
+      hipLaunchKernelGGL(gather_segments, dim3((unsigned)chunks), dim3(kGatherThreads), 0, s,
+                         reinterpret_cast<const Segment*>(pool), (int)segs.size());
       e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipStreamSynchronize(s);

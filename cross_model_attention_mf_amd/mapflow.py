@@ -301,10 +301,11 @@ class MapCache:
         h = ctypes.c_void_p()
         _check(lib().mf_map_cache_create(ctypes.byref(self.desc), _ptr(self.pool), pool_bytes, ctypes.byref(h)))
         self.h = h
+        self._destroy = lib().mf_map_cache_destroy  # kept for interpreter shutdown
 
     def close(self):
         if getattr(self, "h", None):
-            lib().mf_map_cache_destroy(self.h)
+            self._destroy(self.h)
             self.h = None
 
     __del__ = close
