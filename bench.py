@@ -48,7 +48,138 @@ def parse():
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="only time whole-sequence compression against cached prefix + suffix + splice")
+    ap.add_argument("--several-receivers", action="store_true",
+                    help="only time the 32K one-sender / two-receiver fused step three ways")
     return ap.parse_args()
+
+
+def _event_ms(fn, reps: int) -> float:
+    import torch
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def prefix_cache_bench(reps: int, tau: float):
+    """8K, 16 layers: compression of the whole sequence vs compression of the
+    rows after m cached row-blocks plus the splice (host work included)."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(3)
+    L, B = wl.num_layers, wl.B
+    lay = synth.batch_layout(wl)
+    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(L)]
+    q = torch.stack([x.q for x in ins]).to(dev)
+    k = torch.stack([x.k for x in ins]).to(dev)
+    del ins
+    T = k.shape[1]
+
+    def sender(q0):
+        batch = mf.Batch([0, T - q0], [0, T], [q0] if q0 else None, B)
+        qs = q[:, q0:].contiguous()
+        cap = pipeline.count_capacity(batch, qs, k, B, tau)
+        st = pipeline.alloc_sender(batch, qs, k, B, cap)
+
+        def run():
+            mf.block_stats(st.desc, batch, qs, k, st.row_lse, st.block_mass, st.stats_workspace)
+            mf.compress_blocks(st.desc, batch, qs, k, st.row_lse, st.block_mass, tau, st.row_ptr, st.col_idx,
+                               st.values, cap, st.workspace, sync_count=False)
+        ms = _event_ms(run, reps)
+        st.nnz = cap
+        return st, ms
+
+    full, t_full = sender(0)
+    nb = full.batch.total_rowblocks
+    keys = mf.prefix_block_hashes(np.random.default_rng(1).integers(0, 50000, T, dtype=np.int32), B)
+    cache = mf.MapCache(q.dtype, L, wl.H_s, B, full.nnz * (B * B * 2 + 4) + (64 << 20))
+    t0 = time.perf_counter()
+    cache.insert(keys, full.row_ptr.cpu().numpy(), nb, 0, full.col_idx, full.values)
+    t_ins = (time.perf_counter() - t0) * 1e3
+    rp, ci, vals = torch.empty_like(full.row_ptr), torch.empty_like(full.col_idx), torch.empty_like(full.values)
+    rows = []
+    for m in (nb // 4, nb // 2, 3 * nb // 4, nb - nb // 16, nb):
+        suf, t_suf = sender(m * B) if m < nb else (None, 0.0)
+        assert cache.lookup(keys[:m]) == m
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if suf is None:
+                nnz = cache.splice(keys[:m], m, nb, None, 0, 0, None, None, rp, ci, vals)
+            else:
+                nnz = cache.splice(keys[:m], m, nb, suf.row_ptr.cpu().numpy(), suf.batch.total_rowblocks, 0,
+                                   suf.col_idx, suf.values, rp, ci, vals)
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        cache.release(keys[:m], m)
+        same = (nnz == full.nnz and torch.equal(rp, full.row_ptr) and torch.equal(ci, full.col_idx)
+                and torch.equal(vals, full.values))
+        t_spl = float(np.median(ts))
+        rows.append({"cached_rowblocks": m, "suffix_compress_ms": round(t_suf, 3), "splice_ms": round(t_spl, 3),
+                     "total_ms": round(t_suf + t_spl, 3), "bit_exact": bool(same)})
+    print(json.dumps({"metric": "prefix cache: compression time with m of n row-blocks cached",
+                      "config": {"workload": "bf16 causal 8192 tokens, 16 layers, sender 32 heads, d=128, B=64",
+                                 "tau": tau, "rowblocks": nb, "kept_blocks": full.nnz},
+                      "whole_sequence_ms": round(t_full, 3), "insert_ms": round(t_ins, 3), "rows": rows}))
+
+
+def several_receivers_bench(reps: int):
+    """32K, one 40-head sender, receivers of 32 and 24 heads: one launch per
+    receiver on one stream, on two streams, and one launch for both."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(5)
+    lay = synth.batch_layout(wl)
+    x = synth.layer_inputs(wl, 0, layout=lay)
+    q, k = x.q[None].to(dev), x.k[None].to(dev)
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    cap = pipeline.count_capacity(batch, q, k, wl.B, wl.tau)
+    st = pipeline.compress(pipeline.alloc_sender(batch, q, k, wl.B, cap), q, k, wl.tau)
+    recv = [(x.w[None].to(dev), x.v[None].to(dev))]
+    recv += [(w[None].to(dev), v[None].to(dev)) for w, v in zip(x.extra_w, x.extra_v)]
+    ss = [torch.cuda.Stream() for _ in recv]
+
+    def one_stream():
+        return [pipeline.mapped(st, W, v, [0]) for W, v in recv]
+
+    def two_streams():
+        cur, outs = torch.cuda.current_stream(), []
+        for s in ss:
+            s.wait_stream(cur)
+        for (W, v), s in zip(recv, ss):
+            with torch.cuda.stream(s):
+                outs.append(pipeline.mapped(st, W, v, [0], stream=s))
+        for s in ss:
+            cur.wait_stream(s)
+        return outs
+
+    def one_launch():
+        return pipeline.mapped_multi(st, recv, [0])
+
+    ref = one_stream()
+    res = {}
+    for name, f in (("one_launch_per_receiver_one_stream", one_stream),
+                    ("one_launch_per_receiver_two_streams", two_streams), ("one_launch_for_both", one_launch)):
+        o = f()
+        torch.cuda.synchronize()
+        res[name] = {"ms": round(_event_ms(f, reps), 3), "same_as_one_stream": all(torch.equal(a, b) for a, b in zip(o, ref))}
+    print(json.dumps({"metric": "fused mapped attention.V for two receivers of one compressed map",
+                      "config": {"workload": "bf16 causal 32768 tokens, sender 40 heads, d=128, B=128, receivers 32 and 24 heads",
+                                 "tau": wl.tau, "kept_blocks": st.nnz,
+                                 "kept_value_bytes": st.nnz * wl.B * wl.B * 2},
+                      "results": res}))
 
 
 def source_hash(rel: str) -> str:
@@ -118,6 +249,13 @@ def main():
         from cross_model_attention_mf_amd import build_lib
         build_lib.build()
     dev = torch.device("cuda")
+
+    if args.prefix_cache:
+        prefix_cache_bench(max(args.steps, 3), args.tau)
+        return
+    if args.several_receivers:
+        several_receivers_bench(max(args.steps, 3))
+        return
 
     if args.copy_calibration:
         n = 1 << 30
