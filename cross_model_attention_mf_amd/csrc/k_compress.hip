@@ -90,7 +90,124 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a, int n
   if (tid == 0) a.counts[row] = kstar;
 }
 
+// One wave per CSR row for rows of at most 64 * E candidates: the keys sit
+// in registers (element e of lane L is sorted position L + 64 e), the bitonic
+// network exchanges across lanes with shuffles and inside a lane for strides
+// of 64 and up, the fp64 cumulative sum is a wave scan per element, and the
+// kept set is every key at or before the cut key, so the bit words come
+// straight from ballots over the unsorted keys.
+constexpr int kSelWaves = 4;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, mask, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), mask, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)x, src, 64);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(x >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double key_mass(uint64_t key) {
+  return (double)__uint_as_float(0xFFFFFFFFu - (uint32_t)(key >> 32));
+}
+
+template <int E>
+__global__ void __launch_bounds__(kSelWaves * 64) select_wave_kernel(SelectArgs a, long long nrows) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * kSelWaves + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // uniform per wave
+  const int rb = (int)(row % a.b.total_rb);
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, a.B, rb);
+  const int n = ri.ncand;
+  const float* __restrict__ m = a.block_mass + row * (long long)a.b.max_cb;
+
+  uint64_t orig[E], key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = lane + 64 * e;
+    orig[e] = t < n ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(m[t])) << 32) | (uint32_t)t : ~0ull;
+    key[e] = orig[e];
+  }
+  // bitonic sort, ascending keys = mass descending, column ascending
+#pragma unroll
+  for (int k = 2; k <= 64 * E; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= 64) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int f = e ^ (jj >> 6);
+          if (f > e) {
+            const bool up = ((lane + 64 * e) & k) == 0;
+            const uint64_t x = key[e], y = key[f];
+            const uint64_t lo = x < y ? x : y, hi = x < y ? y : x;
+            key[e] = up ? lo : hi;
+            key[f] = up ? hi : lo;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t y = shfl_xor_u64(key[e], jj);
+          const bool lower = (lane & jj) == 0;
+          const bool up = ((lane + 64 * e) & k) == 0;
+          const uint64_t x = key[e];
+          key[e] = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+        }
+      }
+    }
+  }
+  // shortest sorted prefix whose fp64 cumulative mass reaches tau
+  int kstar = n;
+  if (a.tau < 1.0) {
+    double run = 0.0;
+    bool found = false;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool valid = lane + 64 * e < n;
+      double c = valid ? key_mass(key[e]) : 0.0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(c, off, 64);
+        if (lane >= off) c += y;
+      }
+      c += run;
+      run = __shfl(c, 63, 64);
+      const unsigned long long hit = __ballot(valid && c >= a.tau);
+      if (!found && hit) {
+        kstar = 64 * e + __ffsll((long long)hit);
+        found = true;
+      }
+    }
+  }
+  // kept = every candidate whose key is at or before the cut key
+  uint64_t cut = 0;
+  if (kstar > 0) {
+    const int r = kstar - 1;
+    uint64_t src = key[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e)
+      if ((r >> 6) == e) src = key[e];
+    cut = shfl_u64(src, r & 63);
+  }
+  uint32_t* __restrict__ out = a.keep_bits + row * (long long)a.words;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const unsigned long long bal = __ballot(kstar > 0 && orig[e] <= cut);
+    if (lane == 0) {
+      if (2 * e < a.words) out[2 * e] = (uint32_t)bal;
+      if (2 * e + 1 < a.words) out[2 * e + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  if (lane == 0) a.counts[row] = kstar;
+}
+
+// Exclusive scan of the per-row counts into row_ptr by one workgroup: tiles
+// of 1024 x 32 counts, each thread scanning 32 consecutive counts in
+// registers, then one wave-and-LDS scan of the 1024 thread totals per tile.
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 32;
 
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
   __shared__ long long wsum[kScanThreads / 64];
@@ -98,11 +215,16 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) carry_s = 0;
   __syncthreads();
-  for (int64_t base = 0; base < a.n; base += kScanThreads) {
-    const int64_t i = base + tid;
-    const long long x = i < a.n ? a.counts[i] : 0;
-    // inclusive scan inside the wave
-    long long v = x;
+  for (int64_t base = 0; base < a.n; base += (int64_t)kScanThreads * kScanPer) {
+    const int64_t i0 = base + (int64_t)tid * kScanPer;
+    int32_t x[kScanPer];
+    long long tot = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      x[u] = i0 + u < a.n ? a.counts[i0 + u] : 0;
+      tot += x[u];
+    }
+    long long v = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const long long y = __shfl_up(v, off, 64);
@@ -110,12 +232,16 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
     }
     if (lane == 63) wsum[w] = v;
     __syncthreads();
-    long long pre = 0;
+    long long pre = carry_s;
     for (int u = 0; u < w; ++u) pre += wsum[u];
-    const long long carry = carry_s;
-    if (i < a.n) a.row_ptr[i] = (int32_t)(carry + pre + v - x);
+    long long run = pre + v - tot;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      if (i0 + u < a.n) a.row_ptr[i0 + u] = (int32_t)run;
+      run += x[u];
+    }
     __syncthreads();
-    if (tid == kScanThreads - 1) carry_s = carry + pre + v;
+    if (tid == kScanThreads - 1) carry_s = run;
     __syncthreads();
   }
   if (tid == 0) {
@@ -450,6 +576,14 @@ size_t select_lds_bytes(int max_cb) {
 int launch_select(const SelectArgs& a, void* stream) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
   const int n2 = next_pow2(a.b.max_cb < 1 ? 1 : a.b.max_cb);
+  const char* env = getenv("MF_PORTABLE_SELECT");
+  if (n2 <= 256 && !(env && env[0] == '1')) {
+    const long long nrows = (long long)a.L * a.H * a.b.total_rb;
+    const dim3 grid((unsigned)((nrows + kSelWaves - 1) / kSelWaves));
+    auto kern = n2 <= 64 ? select_wave_kernel<1> : n2 <= 128 ? select_wave_kernel<2> : select_wave_kernel<4>;
+    hipLaunchKernelGGL(kern, grid, dim3(kSelWaves * 64), 0, (hipStream_t)stream, a, nrows);
+    return (int)hipGetLastError();
+  }
   const size_t lds = select_lds_bytes(a.b.max_cb);
   hipError_t e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return (int)e;

@@ -219,3 +219,24 @@ def test_portable_and_mfma_block_stats_agree_with_oracle(monkeypatch, d):
     (lse_p, mass_p), (lse_f, mass_f) = results
     assert torch.allclose(lse_p, lse_f, rtol=0, atol=1e-4)
     assert float((mass_p - mass_f).abs().max()) <= 2e-6
+
+
+@pytest.mark.parametrize("B,seqlens", [(64, (64 * 9 + 17, 63, 700)),          # up to 64 candidates per row
+                                       (32, (32 * 120 + 5, 40)),              # up to 128
+                                       (32, (32 * 250 + 31, 32 * 3))])         # up to 256
+def test_wave_and_workgroup_selection_agree(monkeypatch, B, seqlens):
+    """The one-wave-per-row selection and the workgroup sort give the same
+    CSR; the run is also checked against the oracle."""
+    wl = tiny_structured("bf16", workload_id=16, B=B, d=64, H_s=6, H_r=4, seqlens=seqlens)
+    runs = []
+    for portable in ("1", "0"):
+        monkeypatch.setenv("MF_PORTABLE_SELECT", portable)
+        for tau in (0.5, 0.95):
+            runs.append(parity.run_gpu(wl, tau, [0]))
+    nrb = runs[-1].state.batch.total_rowblocks
+    parity.check_layer(runs[-1], 0, rowblocks=parity.sample_rowblocks(nrb, 12))
+    for a, b in zip(runs[:2], runs[2:]):
+        assert a.state.nnz == b.state.nnz
+        assert torch.equal(a.state.row_ptr, b.state.row_ptr)
+        assert torch.equal(a.state.col_idx, b.state.col_idx)
+        assert torch.equal(a.state.values, b.state.values)
