@@ -50,6 +50,8 @@ def parse():
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--prefix-cache", action="store_true",
                     help="only time whole-sequence compression against cached prefix + suffix + splice")
+    ap.add_argument("--fetch-overlap", action="store_true",
+                    help="only time a cache fetch overlapped with a stand-in for the receiver's early layers")
     ap.add_argument("--several-receivers", action="store_true",
                     help="only time the 32K one-sender / two-receiver fused step three ways")
     return ap.parse_args()
@@ -131,6 +133,87 @@ def prefix_cache_bench(reps: int, tau: float):
                       "config": {"workload": "bf16 causal 8192 tokens, 16 layers, sender 32 heads, d=128, B=64",
                                  "tau": tau, "rowblocks": nb, "kept_blocks": full.nnz},
                       "whole_sequence_ms": round(t_full, 3), "insert_ms": round(t_ins, 3), "rows": rows}))
+
+
+def fetch_overlap_bench(reps: int, tau: float):
+    """8K, 16 mapped layers: fetching a fully cached sequence's compressed
+    maps (the splice, HBM-bound) on a second stream while the receiver
+    recomputes its 8 unmapped early layers.  The recompute stand-in is block
+    statistics over receiver-shaped Q/K (24 heads, d = 128): an MFMA-bound
+    causal Q.K^T pass like a dense prefill's attention scores."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(3)
+    L, B = wl.num_layers, wl.B
+    lay = synth.batch_layout(wl)
+    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(L)]
+    q = torch.stack([x.q for x in ins]).to(dev)
+    k = torch.stack([x.k for x in ins]).to(dev)
+    del ins
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, B)
+    cap = pipeline.count_capacity(batch, q, k, B, tau)
+    full = pipeline.compress(pipeline.alloc_sender(batch, q, k, B, cap), q, k, tau)
+    nb = batch.total_rowblocks
+    keys = mf.prefix_block_hashes(np.random.default_rng(1).integers(0, 50000, lay.total_k, dtype=np.int32), B)
+    del q, k
+    # receiver early layers: 8 layers of 24 heads
+    rwl = synth.workload_by_id(3).replace(workload_id=31, H_s=wl.H_r, num_layers=8)
+    rins = [synth.layer_inputs(rwl, l, layout=lay) for l in range(rwl.num_layers)]
+    rq = torch.stack([x.q for x in rins]).to(dev)
+    rk = torch.stack([x.k for x in rins]).to(dev)
+    del rins
+    rst = pipeline.alloc_sender(batch, rq, rk, B, 0)
+
+    def recompute():
+        mf.block_stats(rst.desc, batch, rq, rk, rst.row_lse, rst.block_mass, rst.stats_workspace)
+
+    def wall_ms(fn):
+        ts = []
+        for _ in range(reps + 1):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(ts[1:]))
+
+    recompute()
+    torch.cuda.synchronize()
+    ref_mass = rst.block_mass.clone()
+    rp, ci, vals = torch.empty_like(full.row_ptr), torch.empty_like(full.col_idx), torch.empty_like(full.values)
+    side = torch.cuda.Stream()
+    cache = mf.MapCache(full.values.dtype, L, wl.H_s, B, full.nnz * (B * B * 2 + 4) + (64 << 20))
+    cache.insert(keys, full.row_ptr.cpu().numpy(), nb, 0, full.col_idx, full.values)
+    assert cache.lookup(keys) == nb
+
+    def fetch():
+        return cache.splice(keys, nb, nb, None, 0, 0, None, None, rp, ci, vals)
+
+    def sequential():
+        recompute()
+        fetch()
+
+    def overlapped():
+        pipeline.fetch_overlapped(cache, keys, nb, nb, None, rp, ci, vals, recompute, side)
+
+    out = {name: round(wall_ms(fn), 3) for name, fn in
+           (("fetch_ms", fetch), ("recompute_ms", recompute), ("sequential_ms", sequential),
+            ("overlapped_ms", overlapped))}
+    rp.zero_(); ci.zero_(); vals.zero_(); rst.block_mass.zero_()
+    torch.cuda.synchronize()
+    overlapped()
+    torch.cuda.synchronize()
+    out["bit_exact"] = bool(torch.equal(rp, full.row_ptr) and torch.equal(ci, full.col_idx)
+                            and torch.equal(vals, full.values) and torch.equal(rst.block_mass, ref_mass))
+    cache.release(keys, nb)
+    print(json.dumps({"metric": "cached-map fetch overlapped with the receiver's early-layer recompute",
+                      "config": {"workload": "bf16 causal 8192 tokens; fetch: 16 mapped layers x 32 sender heads, "
+                                             "B=64, all 128 row-blocks cached; recompute stand-in: block statistics "
+                                             "over 8 layers x 24 receiver heads, d=128",
+                                 "tau": tau, "kept_blocks": full.nnz},
+                      "results": out}))
 
 
 def several_receivers_bench(reps: int):
@@ -252,6 +335,9 @@ def main():
 
     if args.prefix_cache:
         prefix_cache_bench(max(args.steps, 3), args.tau)
+        return
+    if args.fetch_overlap:
+        fetch_overlap_bench(max(args.steps, 3), args.tau)
         return
     if args.several_receivers:
         several_receivers_bench(max(args.steps, 3))

@@ -116,7 +116,19 @@ struct mf_map_cache {
   uint64_t clock = 0;
   mf_map_cache_stats st{};
   std::vector<Segment> segs;
-  std::vector<int32_t> rp;          // host staging of a spliced row_ptr
+  std::vector<int32_t> rp;          // a spliced row_ptr, built on the host
+  // pinned host staging of the segment table and row_ptr, so the copies to
+  // the device are asynchronous; `staged` marks when they have been read
+  char* hstage = nullptr;
+  size_t hstage_bytes = 0;
+  hipEvent_t staged = nullptr;
+  bool in_flight = false;
+
+  ~mf_map_cache() {
+    if (in_flight) (void)hipEventSynchronize(staged);
+    if (staged) (void)hipEventDestroy(staged);
+    if (hstage) (void)hipHostFree(hstage);
+  }
 
   bool alloc(size_t bytes, size_t* off) {
     for (auto it = free_ranges.begin(); it != free_ranges.end(); ++it) {
@@ -184,8 +196,30 @@ struct mf_map_cache {
     }
     return want_pinned ? nullptr : any;
   }
-  mf_status run_segments(void* stream, const char* fn) {
-    if (segs.empty()) return MF_OK;
+  // The staging area may be rewritten once the previous call's host-to-device
+  // copies have read it.
+  mf_status stage_room(size_t need, const char* fn) {
+    hipError_t e = hipSuccess;
+    if (in_flight) {
+      e = hipEventSynchronize(staged);
+      in_flight = false;
+    }
+    if (e == hipSuccess && !staged) e = hipEventCreateWithFlags(&staged, hipEventDisableTiming);
+    if (e == hipSuccess && need > hstage_bytes) {
+      const size_t want = need > 2 * hstage_bytes ? need : 2 * hstage_bytes;
+      if (hstage) e = hipHostFree(hstage);
+      hstage = nullptr;
+      hstage_bytes = 0;
+      if (e == hipSuccess) e = hipHostMalloc((void**)&hstage, want, hipHostMallocDefault);
+      if (e == hipSuccess) hstage_bytes = want;
+    }
+    if (e != hipSuccess) return fail(MF_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return MF_OK;
+  }
+  // Stream-ordered: the segment table (and a row_ptr for rp_dst) go through
+  // the pinned staging area to the device, then one gather launch copies
+  // every segment.  Nothing waits for the device.
+  mf_status run_segments(void* stream, const char* fn, int32_t* rp_dst = nullptr) {
     const size_t bytes = segs.size() * sizeof(Segment);
     if (bytes > table_bytes) return fail(MF_ERR_UNSUPPORTED, "%s: %zu copy segments exceed the table", fn, segs.size());
     uint64_t chunks = 0;
@@ -193,17 +227,30 @@ struct mf_map_cache {
       sg.first = chunks;
       chunks += (sg.bytes + kChunk - 1) / kChunk;
     }
-    if (chunks == 0) return MF_OK;
     if (chunks > 0x7fffffffull) return fail(MF_ERR_UNSUPPORTED, "%s: %llu bytes to copy in one call", fn,
                                             (unsigned long long)(chunks * kChunk));
+    const size_t rp_bytes = rp_dst ? rp.size() * sizeof(int32_t) : 0;
+    const size_t rp_off = align256(bytes);
+    if (chunks == 0 && rp_bytes == 0) return MF_OK;
+    mf_status st = stage_room(rp_off + rp_bytes, fn);
+    if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hipMemcpyAsync(pool, segs.data(), bytes, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) {
+    hipError_t e = hipSuccess;
+    if (chunks) {
+      memcpy(hstage, segs.data(), bytes);
+      e = hipMemcpyAsync(pool, hstage, bytes, hipMemcpyHostToDevice, s);
+    }
+    if (e == hipSuccess && rp_bytes) {
+      memcpy(hstage + rp_off, rp.data(), rp_bytes);
+      e = hipMemcpyAsync(rp_dst, hstage + rp_off, rp_bytes, hipMemcpyHostToDevice, s);
+    }
+    if (e == hipSuccess) e = hipEventRecord(staged, s);
+    if (e == hipSuccess) in_flight = true;
+    if (e == hipSuccess && chunks) {
       hipLaunchKernelGGL(gather_segments, dim3((unsigned)chunks), dim3(kGatherThreads), 0, s,
                          reinterpret_cast<const Segment*>(pool), (int)segs.size());
       e = hipGetLastError();
     }
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(MF_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     return MF_OK;
   }
@@ -418,10 +465,8 @@ mf_status mf_map_cache_splice(mf_map_cache* c, const uint64_t* hashes, int32_t m
       }
     }
   }
-  hipError_t he = hipMemcpyAsync(row_ptr_out, c->rp.data(), c->rp.size() * 4, hipMemcpyHostToDevice, (hipStream_t)stream);
-  if (he != hipSuccess) return fail(MF_ERR_HIP, "%s: %s", fn, hipGetErrorString(he));
   if (e) e->last_use = ++c->clock;
-  return c->run_segments(stream, fn);
+  return c->run_segments(stream, fn, row_ptr_out);
 }
 
 mf_status mf_map_cache_get_stats(const mf_map_cache* c, mf_map_cache_stats* out) {

@@ -114,3 +114,35 @@ def mapped_multi(st: SenderState, receivers: Sequence[tuple], layer_map: Sequenc
         Ws.append(W); vs.append(v); outs.append(out)
     mf.mapped_attn_v_multi(descs, st.batch, st.row_ptr, st.col_idx, st.values, Ws, vs, outs, stream)
     return outs
+
+
+def fetch_overlapped(cache: mf.MapCache, keys, m: int, n_blocks: int, suffix: Optional[SenderState],
+                     row_ptr_out: torch.Tensor, col_idx_out: torch.Tensor, values_out: torch.Tensor,
+                     recompute, fetch_stream) -> int:
+    """Fetch the cached rows of a sequence (the splice of its first m
+    row-blocks with the suffix's) on `fetch_stream` while `recompute()` runs
+    its work on the current stream; the current stream then waits for the
+    fetch.  The recompute is launched first, so its kernels take their
+    compute units before the copy fills the rest.  Returns the spliced entry
+    count."""
+    cur = torch.cuda.current_stream()
+    ready = torch.cuda.Event()
+    ready.record(cur)
+    suffix_rp = suffix.row_ptr.cpu().numpy() if suffix is not None else None
+    recompute()
+    fetch_stream.wait_event(ready)
+    for t in (row_ptr_out, col_idx_out, values_out):
+        t.record_stream(fetch_stream)
+    if suffix is not None:
+        for t in (suffix.col_idx, suffix.values):
+            t.record_stream(fetch_stream)
+    with torch.cuda.stream(fetch_stream):
+        if suffix is None:
+            nnz = cache.splice(keys[:m], m, n_blocks, None, 0, 0, None, None, row_ptr_out, col_idx_out,
+                               values_out, stream=fetch_stream)
+        else:
+            nnz = cache.splice(keys[:m], m, n_blocks, suffix_rp, suffix.batch.total_rowblocks, 0,
+                               suffix.col_idx, suffix.values, row_ptr_out, col_idx_out, values_out,
+                               stream=fetch_stream)
+    cur.wait_stream(fetch_stream)
+    return nnz

@@ -291,7 +291,17 @@ typedef struct {
  * outlive the cache).  The index stays on the host.  Entries not pinned by a
  * lookup are evicted least recently used first when an insert needs room.
  * One caller at a time, and every call on one stream (or synchronised
- * between streams): the cache reuses a small table area in the pool. */
+ * between streams): the cache reuses a small table area in the pool.
+ *
+ * Insert and splice are stream-ordered and return before their copies run:
+ * their device sources must stay unchanged, and their outputs are ready, only
+ * once `stream` has passed the call.  So a fetch of cached rows can overlap
+ * other work on another stream (the receiver recomputing its early layers
+ * while the maps are fetched: the MapFlow page, paragraph "第二").  A call
+ * waits on the host only for the previous call's small host-to-device table
+ * copies; the cache keeps a pinned host staging buffer for them (allocated at
+ * the first copying call, grown when a larger row_ptr needs it, freed by
+ * mf_map_cache_destroy, which first waits for those copies). */
 mf_status mf_map_cache_create(const mf_map_cache_desc* desc, void* pool, size_t pool_bytes,
                               mf_map_cache** out);
 void mf_map_cache_destroy(mf_map_cache* cache);

@@ -213,3 +213,41 @@ def test_eviction_is_lru_and_skips_pinned_entries():
     assert cache.lookup(kb) == 4
     assert_same_csr(splice(cache, kb, 4, 4, None, b), b)
     cache.close()
+
+
+def test_fetch_overlapped_with_other_work_is_exact():
+    """Splices run stream-ordered on a side stream while other kernels run on
+    the current stream; back-to-back calls reuse the staging area."""
+    B, d, tau = 64, 128, 0.9
+    T = 7 * B + 19
+    wl = seq_workload("bf16", B, d, T, wid=29)
+    q, k = seq_qk(wl)
+    full = compress_rows(q, k, B, tau)
+    keys = mf.prefix_block_hashes(tokens_of(T, 11), B)
+    cache = mf.MapCache(q.dtype, 2, wl.H_s, B, 64 << 20)
+    cache.insert(keys, full.row_ptr.cpu().numpy(), 8, 0, full.col_idx, full.values)
+    # other work: block statistics of another model's Q/K
+    oq, ok = seq_qk(seq_workload("bf16", B, d, 4 * T, wid=30, H_s=6))
+    ob = mf.Batch([0, 4 * T], [0, 4 * T], None, B)
+    ost = pipeline.alloc_sender(ob, oq, ok, B, 0)
+
+    def other():
+        mf.block_stats(ost.desc, ob, oq, ok, ost.row_lse, ost.block_mass, ost.stats_workspace)
+
+    other()
+    torch.cuda.synchronize()
+    ref_mass = ost.block_mass.clone()
+    side = torch.cuda.Stream()
+    for m in (4, 7, 7):
+        assert cache.lookup(keys[:m]) == m
+        suf = compress_rows(q, k, B, tau, m * B)
+        rp = torch.full_like(full.row_ptr, -1)
+        ci = torch.full_like(full.col_idx, -1)
+        vals = torch.zeros_like(full.values)
+        ost.block_mass.zero_()
+        nnz = pipeline.fetch_overlapped(cache, keys, m, 8, suf, rp, ci, vals, other, side)
+        torch.cuda.synchronize()
+        cache.release(keys[:m], m)
+        assert_same_csr((nnz, rp, ci, vals), full)
+        assert torch.equal(ost.block_mass, ref_mass)
+    cache.close()
