@@ -362,3 +362,88 @@ mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_rec
 }
 
 }  // extern "C"
+
+namespace {
+
+mf_status check_headmix(const mf_headmix_desc* d, const char* fn) {
+  if (!d) return fail(MF_ERR_INVALID, "%s: desc is NULL", fn);
+  if (d->dtype != MF_F32 && d->dtype != MF_BF16) return fail(MF_ERR_INVALID, "%s: unknown dtype %d", fn, (int)d->dtype);
+  if (d->B != 32 && d->B != 64 && d->B != 128) return fail(MF_ERR_UNSUPPORTED, "%s: B = %d not in {32, 64, 128}", fn, d->B);
+  if (d->H_s < 1 || d->H_s > 64 || d->H_r < 1 || d->H_r > 64)
+    return fail(MF_ERR_UNSUPPORTED, "%s: H_s = %d, H_r = %d not in [1, 64]", fn, d->H_s, d->H_r);
+  if (d->num_layers < 0 || d->num_layers > MF_MAX_LAYERS)
+    return fail(MF_ERR_INVALID, "%s: num_layers = %d not in [0, %d]", fn, d->num_layers, MF_MAX_LAYERS);
+  if (d->num_layers > 0 && !d->layer_map) return fail(MF_ERR_INVALID, "%s: layer_map is NULL", fn);
+  for (int l = 0; l < d->num_layers; ++l)
+    if (d->layer_map[l] < 0 || d->layer_map[l] >= d->sender_layers)
+      return fail(MF_ERR_INVALID, "%s: layer_map[%d] = %d outside [0, %d)", fn, l, d->layer_map[l], d->sender_layers);
+  if (d->sender_capacity < 0 || d->receiver_capacity < 0) return fail(MF_ERR_INVALID, "%s: negative capacity", fn);
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mf_headmix_workspace_size(const mf_headmix_desc* desc, const mf_batch* batch) {
+  if (!desc || !batch || desc->num_layers < 0 || desc->H_s < 1 || desc->H_s > 64 || desc->H_r < 1 || desc->H_r > 64 ||
+      batch->info.total_rowblocks < 0)
+    return 0;
+  return align256(mf::headmix_partial_bytes(desc->num_layers, batch->info.total_rowblocks, desc->H_s, desc->H_r));
+}
+
+mf_status mf_headmix_gram(const mf_headmix_desc* desc, const mf_batch* batch, const int32_t* s_row_ptr,
+                          const int32_t* s_col_idx, const void* s_values, const int32_t* r_row_ptr,
+                          const int32_t* r_col_idx, const void* r_values, double* gram, double* cross,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_headmix_gram";
+  mf_status st = check_headmix(desc, fn);
+  if (st) return st;
+  st = check_batch(batch, desc->B, fn);
+  if (st) return st;
+  if (desc->num_layers == 0) return MF_OK;
+  if (!gram || !cross) return fail(MF_ERR_INVALID, "%s: gram or cross is NULL", fn);
+  const int R = batch->info.total_rowblocks;
+  if (R > 0) {
+    if (!s_row_ptr || !r_row_ptr) return fail(MF_ERR_INVALID, "%s: a row_ptr is NULL", fn);
+    if (desc->sender_capacity > 0 && (!s_col_idx || !s_values))
+      return fail(MF_ERR_INVALID, "%s: sender col_idx or values is NULL", fn);
+    if (desc->receiver_capacity > 0 && (!r_col_idx || !r_values))
+      return fail(MF_ERR_INVALID, "%s: receiver col_idx or values is NULL", fn);
+    if ((int64_t)desc->sender_layers * desc->H_s * R > INT32_MAX - 1 || (int64_t)desc->num_layers * desc->H_r * R > INT32_MAX - 1)
+      return fail(MF_ERR_UNSUPPORTED, "%s: too many CSR rows", fn);
+  }
+  const size_t need = mf_headmix_workspace_size(desc, batch);
+  if (R > 0 && (!workspace || workspace_bytes < need))
+    return fail(MF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+  if (mf::headmix_gram_lds_bytes(desc->H_s, desc->H_r) > device_lds_limit())
+    return fail(MF_ERR_UNSUPPORTED, "%s: staging does not fit in LDS", fn);
+  mf::HeadmixArgs a;
+  a.b = batch_args(batch);
+  a.s_row_ptr = s_row_ptr; a.s_col = s_col_idx; a.s_val = s_values; a.s_cap = desc->sender_capacity;
+  a.r_row_ptr = r_row_ptr; a.r_col = r_col_idx; a.r_val = r_values; a.r_cap = desc->receiver_capacity;
+  a.partial = static_cast<double*>(workspace);
+  a.L = desc->num_layers; a.Hs = desc->H_s; a.Hr = desc->H_r; a.B = desc->B;
+  for (int l = 0; l < desc->num_layers; ++l) a.layer_map[l] = desc->layer_map[l];
+  const int e = mf::launch_headmix_gram(a, desc->dtype, gram, cross, stream);
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+mf_status mf_headmix_solve(const mf_headmix_desc* desc, const double* gram, const double* cross, double lambda,
+                           float* W, int32_t* dropped, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_headmix_solve";
+  if (!desc) return fail(MF_ERR_INVALID, "%s: desc is NULL", fn);
+  if (desc->H_s < 1 || desc->H_s > 64 || desc->H_r < 1 || desc->H_r > 64)
+    return fail(MF_ERR_UNSUPPORTED, "%s: H_s = %d, H_r = %d not in [1, 64]", fn, desc->H_s, desc->H_r);
+  if (desc->num_layers < 0 || desc->num_layers > MF_MAX_LAYERS)
+    return fail(MF_ERR_INVALID, "%s: num_layers = %d not in [0, %d]", fn, desc->num_layers, MF_MAX_LAYERS);
+  if (!(lambda >= 0.0) || isinf(lambda)) return fail(MF_ERR_INVALID, "%s: lambda must be finite and >= 0", fn);
+  if (desc->num_layers == 0) return MF_OK;
+  if (!gram || !cross || !W) return fail(MF_ERR_INVALID, "%s: gram, cross or W is NULL", fn);
+  const int e = mf::launch_headmix_solve(gram, cross, lambda, desc->num_layers, desc->H_s, desc->H_r, W, dropped, stream);
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
+}  // extern "C"

@@ -108,6 +108,23 @@ struct MappedArgs {
   MappedRecv rx[MF_MAX_RECEIVERS];
 };
 
+// Least-squares fit of the head mix: the two CSRs, the layer pairing and
+// the per-row-block partial products (workspace).
+struct HeadmixArgs {
+  BatchArgs b;
+  const int32_t* s_row_ptr;
+  const int32_t* s_col;
+  const void* s_val;
+  int64_t s_cap;
+  const int32_t* r_row_ptr;
+  const int32_t* r_col;
+  const void* r_val;
+  int64_t r_cap;
+  double* partial;          // [L][total_rb][H_s + H_r][H_s]
+  int32_t L, Hs, Hr, B;
+  int32_t layer_map[MF_MAX_LAYERS];
+};
+
 // Launchers: return 0 on success, a hipError_t value otherwise.
 int launch_block_stats(const StatsArgs& a, mf_dtype dt, void* stream);
 size_t block_stats_lds_bytes(int B, int max_cb);
@@ -122,5 +139,10 @@ int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fas
 // all, else one launch per receiver
 int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);
 size_t select_lds_bytes(int max_cb);
+size_t headmix_partial_bytes(int L, int total_rb, int Hs, int Hr);
+size_t headmix_gram_lds_bytes(int Hs, int Hr);
+int launch_headmix_gram(const HeadmixArgs& a, mf_dtype dt, double* gram, double* cross, void* stream);
+int launch_headmix_solve(const double* gram, const double* cross, double lam, int L, int Hs, int Hr, float* W,
+                         int32_t* dropped, void* stream);
 
 }  // namespace mf

@@ -1,0 +1,316 @@
+// Offline calibration of the head mix W by least squares (MapFlow page,
+// section "从内部表示,走向 token 之间的依赖关系": the head mapping is a learned
+// linear combination of sender heads, fitted once offline with both models
+// frozen).  For each receiver layer the fit solves the normal equations
+//   (G + lambda I) w_r = b_r,  G[h][h'] = sum <Pt_h, Pt_h'>,  b_r[h] = sum <A_r, Pt_h>
+// over the blocks (i, j) of the union of the sender heads' kept sets, with
+// Pt_h the kept block of sender head h (0 where h does not keep j) and A_r
+// the receiver head's own block (0 where it does not keep j).
+//
+// headmix_gram_kernel: one workgroup per (receiver layer, row-block).  Wave 0
+// merges the sender heads' sorted column lists (lane h walks head h) and
+// moves each receiver head's list (lane r) up to the union block; the kept
+// blocks of every sender and receiver head are then staged through LDS, 64
+// entries at a time, transposed to [entry][head] in fp32, and each thread
+// accumulates an 8 x 4 tile of [sender + receiver heads] x [sender heads]
+// products in fp64 (bf16 and fp32 products are exact in fp64).  Threads left
+// over split the entries and are summed in a fixed order; each workgroup
+// writes its partial products, and headmix_reduce_kernel adds them over the
+// row-blocks in order, so results do not depend on scheduling.
+// headmix_solve_kernel: one workgroup per layer, Cholesky of G + lambda I in
+// LDS with the drop rule (a pivot at most 1e-12 of its diagonal drops the
+// head: weight 0), then forward and back substitution per receiver head.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace mf {
+namespace {
+
+constexpr int kHmThreads = 256;
+constexpr int kHmChunk = 64;   // block entries staged per step
+constexpr int kNoCol = 0x7FFFFFFF;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+
+struct HmTile {
+  int T, KS;   // tiles, entry slices
+  int CT;      // column tiles
+};
+
+__host__ __device__ inline HmTile hm_tiles(int NA, int Hs) {
+  HmTile t;
+  t.CT = (Hs + 3) / 4;
+  t.T = ((NA + 7) / 8) * t.CT;
+  t.KS = t.T >= kHmThreads ? 1 : kHmThreads / t.T;
+  return t;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int NA = a.Hs + a.Hr;
+  const int NAP = (NA + 7) / 8 * 8;                   // staged heads per entry (padded)
+  float* stage = reinterpret_cast<float*>(smem);      // [kHmChunk][NAP]
+  double* red = reinterpret_cast<double*>(smem);      // reduction (reuses the stage)
+  __shared__ int j_sh;
+  __shared__ unsigned long long smask_sh, rmask_sh;
+  __shared__ long long svidx[64], rvidx[64];
+
+  const int R = a.b.total_rb;
+  const int l = blockIdx.x / R, i = blockIdx.x % R;
+  const int s = a.layer_map[l];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const HmTile tl = hm_tiles(NA, a.Hs);
+  const bool active = tid < tl.T * tl.KS;
+  const int tile = tid % tl.T, ks = tid / tl.T;
+  const int a0 = 8 * (tile / tl.CT), c0 = 4 * (tile % tl.CT);
+  const int BB = a.B * a.B;
+  const T* __restrict__ sval = reinterpret_cast<const T*>(a.s_val);
+  const T* __restrict__ rval = reinterpret_cast<const T*>(a.r_val);
+
+  double acc[8][4];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+
+  // merge state (wave 0): sender list of head `lane`, receiver list of head `lane`
+  long long sp = 0, se = 0, rp = 0, re = 0;
+  int scol = kNoCol, rcol = kNoCol;
+  if (wave == 0) {
+    if (lane < a.Hs) {
+      const size_t row = ((size_t)s * a.Hs + lane) * R + i;
+      sp = min((long long)a.s_row_ptr[row], (long long)a.s_cap);
+      se = min((long long)a.s_row_ptr[row + 1], (long long)a.s_cap);
+      if (sp < se) scol = a.s_col[sp];
+    }
+    if (lane < a.Hr) {
+      const size_t row = ((size_t)l * a.Hr + lane) * R + i;
+      rp = min((long long)a.r_row_ptr[row], (long long)a.r_cap);
+      re = min((long long)a.r_row_ptr[row + 1], (long long)a.r_cap);
+      if (rp < re) rcol = a.r_col[rp];
+    }
+  }
+
+  for (;;) {
+    if (wave == 0) {
+      int jm = scol;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) jm = min(jm, __shfl_xor(jm, off, 64));
+      if (jm != kNoCol) {
+        // receiver heads skip their blocks outside the sender union
+        while (rcol < jm) {
+          ++rp;
+          rcol = rp < re ? a.r_col[rp] : kNoCol;
+        }
+      }
+      const bool take_s = scol == jm && jm != kNoCol;
+      const bool take_r = rcol == jm && jm != kNoCol;
+      const unsigned long long sm = __ballot(take_s), rm = __ballot(take_r);
+      if (take_s) svidx[lane] = sp;
+      if (take_r) rvidx[lane] = rp;
+      if (lane == 0) {
+        j_sh = jm;
+        smask_sh = sm;
+        rmask_sh = rm;
+      }
+      if (take_s) {
+        ++sp;
+        scol = sp < se ? a.s_col[sp] : kNoCol;
+      }
+      if (take_r) {
+        ++rp;
+        rcol = rp < re ? a.r_col[rp] : kNoCol;
+      }
+    }
+    __syncthreads();
+    if (j_sh == kNoCol) break;
+    const unsigned long long sm = smask_sh, rm = rmask_sh;
+    for (int k0 = 0; k0 < BB; k0 += kHmChunk) {
+      // stage entries k0 .. k0 + 63 of every head's block (0 for heads that
+      // do not keep it), consecutive threads on consecutive heads
+      for (int idx = tid; idx < NAP * (kHmChunk / 8); idx += kHmThreads) {
+        const int slot = idx % NAP, part = idx / NAP;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const T* src = nullptr;
+        if (slot < a.Hs) {
+          if ((sm >> slot) & 1ull) src = sval + (size_t)svidx[slot] * BB;
+        } else if (slot < NA) {
+          const int r = slot - a.Hs;
+          if ((rm >> r) & 1ull) src = rval + (size_t)rvidx[r] * BB;
+        }
+        if (src) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = to_f32(src[k0 + 8 * part + e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) stage[(8 * part + e) * NAP + slot] = x[e];
+      }
+      __syncthreads();
+      if (active) {
+        for (int k = ks; k < kHmChunk; k += tl.KS) {
+          const float* row = stage + k * NAP;
+          double xc[4], xr[8];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xc[v] = (double)row[c0 + v];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) xr[u] = (double)row[a0 + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(xr[u], xc[v], acc[u][v]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // sum the entry slices in a fixed order (slice KS - 1 down to 0), then write
+  // this row-block's partial products
+  for (int sl = tl.KS - 1; sl >= 1; --sl) {
+    if (active && ks == sl) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(size_t)tile * 32 + u * 4 + v] = acc[u][v];
+    }
+    __syncthreads();
+    if (active && ks == sl - 1) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] += red[(size_t)tile * 32 + u * 4 + v];
+    }
+    __syncthreads();
+  }
+  if (active && ks == 0) {
+    double* out = a.partial + (size_t)blockIdx.x * NA * a.Hs;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (a0 + u < NA && c0 + v < a.Hs) out[(size_t)(a0 + u) * a.Hs + c0 + v] = acc[u][v];
+  }
+}
+
+// gram[l] / cross[l] = sum over row-blocks i (in order) of the partials
+__global__ void __launch_bounds__(kHmThreads) headmix_reduce_kernel(HeadmixArgs a, double* gram, double* cross) {
+  const int NA = a.Hs + a.Hr;
+  const int e = blockIdx.x * kHmThreads + threadIdx.x, l = blockIdx.y;
+  if (e >= NA * a.Hs) return;
+  const size_t per = (size_t)NA * a.Hs;
+  const double* p = a.partial + (size_t)l * a.b.total_rb * per + e;
+  double t = 0.0;
+  for (int i = 0; i < a.b.total_rb; ++i) t += p[(size_t)i * per];
+  const int row = e / a.Hs, c = e % a.Hs;
+  if (row < a.Hs) gram[((size_t)l * a.Hs + row) * a.Hs + c] = t;
+  else cross[((size_t)l * a.Hr + (row - a.Hs)) * a.Hs + c] = t;
+}
+
+constexpr double kDropTol = 1e-12;
+
+__global__ void __launch_bounds__(64) headmix_solve_kernel(const double* __restrict__ gram,
+                                                           const double* __restrict__ cross, double lam, int Hs,
+                                                           int Hr, float* __restrict__ W, int32_t* __restrict__ dropped) {
+  __shared__ double M[64][65];   // G + lam I, overwritten by its Cholesky factor (lower)
+  __shared__ double Y[64][65];   // per receiver head: y, then w
+  __shared__ double diag0[64];
+  __shared__ int drop[64];
+  const int l = blockIdx.x, t = threadIdx.x;
+  for (int r = 0; r < Hs; ++r)
+    if (t < Hs) M[r][t] = gram[((size_t)l * Hs + r) * Hs + t] + (r == t ? lam : 0.0);
+  __syncthreads();
+  if (t < Hs) diag0[t] = M[t][t];
+  __syncthreads();
+  for (int k = 0; k < Hs; ++k) {
+    if (t == 0) {
+      double piv = M[k][k];
+      for (int p = 0; p < k; ++p) piv -= M[k][p] * M[k][p];
+      const bool dk = !(diag0[k] > 0.0) || piv <= kDropTol * diag0[k];
+      drop[k] = dk;
+      M[k][k] = dk ? 0.0 : sqrt(piv);
+    }
+    __syncthreads();
+    const int i = k + 1 + t;
+    if (i < Hs) {
+      if (drop[k]) {
+        M[i][k] = 0.0;
+      } else {
+        double v = M[i][k];
+        for (int p = 0; p < k; ++p) v -= M[i][p] * M[k][p];
+        M[i][k] = v / M[k][k];
+      }
+    }
+    __syncthreads();
+  }
+  if (t < Hr) {
+    const double* b = cross + ((size_t)l * Hr + t) * Hs;
+    for (int k = 0; k < Hs; ++k) {
+      double v = 0.0;
+      if (!drop[k]) {
+        v = b[k];
+        for (int p = 0; p < k; ++p) v -= M[k][p] * Y[t][p];
+        v /= M[k][k];
+      }
+      Y[t][k] = v;
+    }
+    for (int k = Hs - 1; k >= 0; --k) {
+      double v = 0.0;
+      if (!drop[k]) {
+        v = Y[t][k];
+        for (int p = k + 1; p < Hs; ++p) v -= M[p][k] * Y[t][p];
+        v /= M[k][k];
+      }
+      Y[t][k] = v;   // entries above k already hold w
+    }
+    for (int k = 0; k < Hs; ++k) W[((size_t)l * Hr + t) * Hs + k] = (float)Y[t][k];
+  }
+  if (dropped && t < Hs) dropped[(size_t)l * Hs + t] = drop[t];
+}
+
+}  // namespace
+
+size_t headmix_partial_bytes(int L, int total_rb, int Hs, int Hr) {
+  return (size_t)L * total_rb * (size_t)(Hs + Hr) * Hs * sizeof(double);
+}
+
+size_t headmix_gram_lds_bytes(int Hs, int Hr) {
+  const int NA = Hs + Hr, NAP = (NA + 7) / 8 * 8;
+  const HmTile tl = hm_tiles(NA, Hs);
+  const size_t st = (size_t)kHmChunk * NAP * sizeof(float);
+  const size_t rd = tl.KS > 1 ? (size_t)tl.T * 32 * sizeof(double) : 0;
+  return st > rd ? st : rd;
+}
+
+int launch_headmix_gram(const HeadmixArgs& a, mf_dtype dt, double* gram, double* cross, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int NA = a.Hs + a.Hr;
+  if (a.L == 0) return 0;
+  if (a.b.total_rb > 0) {
+    const size_t lds = headmix_gram_lds_bytes(a.Hs, a.Hr);
+    auto kern = dt == MF_BF16 ? headmix_gram_kernel<__hip_bfloat16> : headmix_gram_kernel<float>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.L * a.b.total_rb)), dim3(kHmThreads), lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  hipLaunchKernelGGL(headmix_reduce_kernel, dim3((unsigned)((NA * a.Hs + kHmThreads - 1) / kHmThreads), (unsigned)a.L),
+                     dim3(kHmThreads), 0, s, a, gram, cross);
+  return (int)hipGetLastError();
+}
+
+int launch_headmix_solve(const double* gram, const double* cross, double lam, int L, int Hs, int Hr, float* W,
+                         int32_t* dropped, void* stream) {
+  if (L == 0) return 0;
+  hipLaunchKernelGGL(headmix_solve_kernel, dim3((unsigned)L), dim3(64), 0, (hipStream_t)stream, gram, cross, lam, Hs,
+                     Hr, W, dropped);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mf

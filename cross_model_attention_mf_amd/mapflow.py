@@ -25,8 +25,8 @@ EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_compress_workspace_size", "mf_compress_blocks",
            "mf_mapped_attn_v", "mf_mapped_attn_v_multi", "mf_prefix_block_hashes", "mf_map_cache_create",
            "mf_map_cache_destroy", "mf_map_cache_insert", "mf_map_cache_lookup", "mf_map_cache_release",
-           "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_status_string", "mf_last_error_message",
-           "mf_version")
+           "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_headmix_workspace_size", "mf_headmix_gram",
+           "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -60,6 +60,13 @@ class ReceiverDesc(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int64),
                 ("csr_capacity", ctypes.c_int64)]
+
+
+class HeadmixDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("sender_layers", ctypes.c_int32), ("layer_map", _i32p), ("H_s", ctypes.c_int32),
+                ("H_r", ctypes.c_int32), ("sender_capacity", ctypes.c_int64),
+                ("receiver_capacity", ctypes.c_int64)]
 
 
 class MapCacheDesc(ctypes.Structure):
@@ -125,8 +132,14 @@ def lib():
     L.mf_map_cache_splice.argtypes = [vp, u64p, i32, i32, _i32p, i32, i32, vp, vp, vp, vp, vp, i64,
                                       ctypes.POINTER(i64), vp]
     L.mf_map_cache_get_stats.argtypes = [vp, ctypes.POINTER(MapCacheStats)]
+    L.mf_headmix_workspace_size.argtypes = [ctypes.POINTER(HeadmixDesc), ctypes.POINTER(BatchC)]
+    L.mf_headmix_workspace_size.restype = sz
+    L.mf_headmix_gram.argtypes = [ctypes.POINTER(HeadmixDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp, vp, vp,
+                                  vp, vp, vp, sz, vp]
+    L.mf_headmix_solve.argtypes = [ctypes.POINTER(HeadmixDesc), vp, vp, ctypes.c_double, vp, vp, vp]
     for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v", "mf_mapped_attn_v_multi",
-              "mf_map_cache_create", "mf_map_cache_insert", "mf_map_cache_splice", "mf_map_cache_get_stats"):
+              "mf_map_cache_create", "mf_map_cache_insert", "mf_map_cache_splice", "mf_map_cache_get_stats",
+              "mf_headmix_gram", "mf_headmix_solve"):
         getattr(L, f).restype = ctypes.c_int
     L.mf_status_string.argtypes = [ctypes.c_int]
     L.mf_status_string.restype = ctypes.c_char_p
@@ -277,6 +290,32 @@ def mapped_attn_v_multi(descs: Sequence[ReceiverDesc], batch: Batch, row_ptr, co
     op = (ctypes.c_void_p * n)(*[_ptr(x) for x in os_])
     _check(lib().mf_mapped_attn_v_multi(dp, n, ctypes.byref(batch.c), _ptr(row_ptr), _ptr(col_idx),
                                         _ptr(values), wp, vp_, op, _stream(stream)))
+
+
+def headmix_desc(dtype: torch.dtype, B: int, layer_map: Sequence[int], sender_layers: int, H_s: int, H_r: int,
+                 sender_capacity: int, receiver_capacity: int) -> HeadmixDesc:
+    lm = _as_i32(layer_map)
+    desc = HeadmixDesc(dtype_code(dtype), B, lm.shape[0], sender_layers, lm.ctypes.data_as(_i32p), H_s, H_r,
+                       sender_capacity, receiver_capacity)
+    desc._keep = lm  # the layer map must outlive the descriptor
+    return desc
+
+
+def headmix_workspace_size(desc: HeadmixDesc, batch: Batch) -> int:
+    return int(lib().mf_headmix_workspace_size(ctypes.byref(desc), ctypes.byref(batch.c)))
+
+
+def headmix_gram(desc: HeadmixDesc, batch: Batch, s_row_ptr, s_col_idx, s_values, r_row_ptr, r_col_idx, r_values,
+                 gram, cross, workspace, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mf_headmix_gram(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(s_row_ptr), _ptr(s_col_idx),
+                                 _ptr(s_values), _ptr(r_row_ptr), _ptr(r_col_idx), _ptr(r_values), _ptr(gram),
+                                 _ptr(cross), _ptr(workspace), ws, _stream(stream)))
+
+
+def headmix_solve(desc: HeadmixDesc, gram, cross, lam: float, W, dropped=None, stream=None):
+    _check(lib().mf_headmix_solve(ctypes.byref(desc), _ptr(gram), _ptr(cross), float(lam), _ptr(W), _ptr(dropped),
+                                  _stream(stream)))
 
 
 def prefix_block_hashes(tokens, B: int, parent: int = 0) -> np.ndarray:

@@ -146,3 +146,23 @@ def fetch_overlapped(cache: mf.MapCache, keys, m: int, n_blocks: int, suffix: Op
                                stream=fetch_stream)
     cur.wait_stream(fetch_stream)
     return nnz
+
+
+def fit_headmix(sender: SenderState, receiver: SenderState, layer_map: Sequence[int], lam: float = 0.0,
+                stream=None):
+    """Least-squares head mix from a sender's and a receiver's compressed maps
+    of one batch.  Returns (W [L_r, H_r, H_s] fp32, dropped [L_r, H_s] int32,
+    G [L_r, H_s, H_s] fp64, b [L_r, H_r, H_s] fp64)."""
+    L_r, H_s, H_r = len(layer_map), sender.desc.H_s, receiver.desc.H_s
+    dev = sender.row_ptr.device
+    desc = mf.headmix_desc(sender.values.dtype, sender.B, layer_map, sender.desc.num_layers, H_s, H_r,
+                           sender.col_idx.numel(), receiver.col_idx.numel())
+    G = torch.empty((L_r, H_s, H_s), dtype=torch.float64, device=dev)
+    b = torch.empty((L_r, H_r, H_s), dtype=torch.float64, device=dev)
+    ws = torch.empty(max(mf.headmix_workspace_size(desc, sender.batch), 1), dtype=torch.uint8, device=dev)
+    mf.headmix_gram(desc, sender.batch, sender.row_ptr, sender.col_idx, sender.values, receiver.row_ptr,
+                    receiver.col_idx, receiver.values, G, b, ws, stream)
+    W = torch.empty((L_r, H_r, H_s), dtype=torch.float32, device=dev)
+    dropped = torch.empty((L_r, H_s), dtype=torch.int32, device=dev)
+    mf.headmix_solve(desc, G, b, lam, W, dropped, stream)
+    return W, dropped, G, b

@@ -249,6 +249,71 @@ mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_rec
                                  void* const* o, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Offline calibration of the head mix                                      */
+/* ------------------------------------------------------------------------ */
+
+/* The head mapping W is a learned linear combination of sender heads,
+ * trained once by offline calibration with both models frozen (section
+ * "从内部表示…").  These calls fit it by least squares from compressed maps:
+ * for receiver layer l, paired with sender CSR layer layer_map[l], W[l]
+ * minimises
+ *     sum_r sum_(i, j) || A_r[i][j] - sum_h W[r][h] Pt_h[i][j] ||_F^2
+ *     + lambda ||W[l]||_F^2
+ * over the blocks (i, j) of the union of the sender heads' kept sets, where
+ * Pt_h[i][j] is sender head h's kept block (0 where h does not keep j; the
+ * operand mf_mapped_attn_v mixes) and A_r[i][j] is receiver head r's block
+ * from the receiver's own compressed map (0 where r does not keep j).  Blocks
+ * outside the union add a constant and are left out.  The minimiser solves
+ *     (G + lambda I) w_r = b_r,  G[h][h'] = sum <Pt_h, Pt_h'>,
+ *                                b_r[h]   = sum <A_r, Pt_h>
+ * (inner products over the B x B entries of a block). */
+typedef struct {
+  mf_dtype dtype;             /* of both CSRs' values */
+  int32_t B;
+  int32_t num_layers;         /* receiver layers fitted = layers of the receiver CSR */
+  int32_t sender_layers;      /* layers of the sender CSR */
+  const int32_t* layer_map;   /* HOST [num_layers]: sender layer of each receiver layer */
+  int32_t H_s, H_r;           /* heads of the sender CSR and of the receiver CSR, each in [1, 64] */
+  int64_t sender_capacity;    /* entries of the sender col_idx / values; entries past it are ignored */
+  int64_t receiver_capacity;  /* same for the receiver CSR */
+} mf_headmix_desc;
+
+/* Workspace bytes of mf_headmix_gram: one partial product matrix per
+ * (receiver layer, row-block), 8 (H_s + H_r) H_s bytes each. */
+size_t mf_headmix_workspace_size(const mf_headmix_desc* desc, const mf_batch* batch);
+
+/* G and b of the normal equations, summed in fp64 (bf16 and fp32 products are
+ * exact in fp64; the sum over row-blocks runs in a fixed order, so results
+ * repeat bit for bit).
+ *   s_row_ptr, s_col_idx, s_values  DEVICE sender CSR as mf_compress_blocks
+ *                                   writes it (sender_layers x H_s rows per
+ *                                   row-block of `batch`)
+ *   r_row_ptr, r_col_idx, r_values  DEVICE receiver CSR of the same batch
+ *                                   layout (num_layers x H_r heads), e.g.
+ *                                   mf_compress_blocks on the receiver's Q/K
+ *   gram   DEVICE fp64 [num_layers][H_s][H_s], overwritten
+ *   cross  DEVICE fp64 [num_layers][H_r][H_s]: cross[l][r][h] = b_r[h]
+ *   workspace  DEVICE, at least mf_headmix_workspace_size() bytes
+ * Both CSRs must use the same B and dtype. */
+mf_status mf_headmix_gram(const mf_headmix_desc* desc, const mf_batch* batch,
+                          const int32_t* s_row_ptr, const int32_t* s_col_idx, const void* s_values,
+                          const int32_t* r_row_ptr, const int32_t* r_col_idx, const void* r_values,
+                          double* gram, double* cross, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* W[l] from gram[l] and cross[l]: a Cholesky factorisation of G + lambda I
+ * in fp64, column by column; head k is dropped when its pivot falls to at
+ * most 1e-12 of its diagonal (a head that keeps nothing, or whose maps lie in
+ * the span of earlier heads) and gets weight 0, the others being the fit
+ * without it.  Then a forward and a back substitution per receiver head.
+ *   gram, cross  DEVICE as written by mf_headmix_gram
+ *   lambda       ridge weight, finite and >= 0
+ *   W            DEVICE fp32 [num_layers][H_r][H_s], ready for mf_mapped_attn_v
+ *   dropped      DEVICE int32 [num_layers][H_s] or NULL: 1 for a dropped head */
+mf_status mf_headmix_solve(const mf_headmix_desc* desc, const double* gram, const double* cross,
+                           double lambda, float* W, int32_t* dropped, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Prefix cache of compressed maps                                          */
 /* ------------------------------------------------------------------------ */
 /* Requests that share a token prefix share the sender's compressed rows for

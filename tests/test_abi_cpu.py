@@ -43,6 +43,7 @@ def _c_layout(tmp_path):
         "mf_receiver_desc": [f for f, _ in mf.ReceiverDesc._fields_],
         "mf_map_cache_desc": [f for f, _ in mf.MapCacheDesc._fields_],
         "mf_map_cache_stats": [f for f, _ in mf.MapCacheStats._fields_],
+        "mf_headmix_desc": [f for f, _ in mf.HeadmixDesc._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mapflow.h"', 'int main(void) {']
     for st, fs in fields.items():
@@ -62,7 +63,8 @@ def test_struct_layouts_match_header(tmp_path):
     c = _c_layout(tmp_path)
     for name, cls in [("mf_plan_info", mf.PlanInfo), ("mf_batch", mf.BatchC),
                       ("mf_sender_desc", mf.SenderDesc), ("mf_receiver_desc", mf.ReceiverDesc),
-                      ("mf_map_cache_desc", mf.MapCacheDesc), ("mf_map_cache_stats", mf.MapCacheStats)]:
+                      ("mf_map_cache_desc", mf.MapCacheDesc), ("mf_map_cache_stats", mf.MapCacheStats),
+                      ("mf_headmix_desc", mf.HeadmixDesc)]:
         assert c[(name, "sizeof")] == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert c[(name, f)] == getattr(cls, f).offset, (name, f)
@@ -284,3 +286,37 @@ def test_map_cache_host_paths():
     assert L.mf_map_cache_create(ctypes.byref(bad), 1 << 20, 1 << 20, ctypes.byref(h)) == mf.MF_ERR_INVALID
     assert L.mf_map_cache_create(ctypes.byref(d), (1 << 20) + 16, 1 << 20, ctypes.byref(h)) == mf.MF_ERR_INVALID
     assert L.mf_map_cache_create(ctypes.byref(d), 1 << 20, 512, ctypes.byref(h)) == mf.MF_ERR_CAPACITY
+
+
+# ---- head-mix fit: argument checks come before any launch
+
+def test_headmix_validation_paths():
+    L = mf.lib()
+    info, plan = mf.plan([0, 200], [0, 200], None, 64)
+    fake = 1 << 20   # never dereferenced: every call below fails validation or has no work
+    bc = mf.BatchC(info, fake, fake, None, fake)
+    good = mf.headmix_desc(torch.bfloat16, 64, [1, 0], 2, 8, 6, 100, 100)
+    need = L.mf_headmix_workspace_size(ctypes.byref(good), ctypes.byref(bc))
+    assert need == -(-2 * info.total_rowblocks * (8 + 6) * 8 * 8 // 256) * 256   # fp64 partials, 256-byte rounded
+
+    def gram(desc, ws=fake, ws_bytes=None, gram_ptr=fake):
+        return L.mf_headmix_gram(ctypes.byref(desc), ctypes.byref(bc), fake, fake, fake, fake, fake, fake,
+                                 gram_ptr, fake, ws, need if ws_bytes is None else ws_bytes, None)
+    assert gram(mf.headmix_desc(torch.bfloat16, 48, [0], 1, 8, 6, 1, 1)) == mf.MF_ERR_UNSUPPORTED
+    assert gram(mf.headmix_desc(torch.bfloat16, 64, [0], 1, 65, 6, 1, 1)) == mf.MF_ERR_UNSUPPORTED
+    assert gram(mf.headmix_desc(torch.bfloat16, 64, [2], 2, 8, 6, 1, 1)) == mf.MF_ERR_INVALID
+    assert gram(mf.headmix_desc(torch.bfloat16, 64, [0], 1, 8, 6, -1, 1)) == mf.MF_ERR_INVALID
+    assert gram(mf.headmix_desc(torch.bfloat16, 32, [0], 1, 8, 6, 1, 1)) == mf.MF_ERR_INVALID  # batch planned for 64
+    assert gram(good, ws_bytes=need - 1) == mf.MF_ERR_WORKSPACE
+    assert gram(good, gram_ptr=None) == mf.MF_ERR_INVALID
+    assert "gram" in L.mf_last_error_message().decode()
+    # no layers: nothing to do
+    assert gram(mf.headmix_desc(torch.bfloat16, 64, [], 2, 8, 6, 1, 1), ws=None, ws_bytes=0) == mf.MF_OK
+
+    def solve(desc, lam=0.0, W=fake):
+        return L.mf_headmix_solve(ctypes.byref(desc), fake, fake, lam, W, None, None)
+    assert solve(good, lam=-1.0) == mf.MF_ERR_INVALID
+    assert solve(good, lam=float("inf")) == mf.MF_ERR_INVALID
+    assert solve(good, lam=float("nan")) == mf.MF_ERR_INVALID
+    assert solve(good, W=None) == mf.MF_ERR_INVALID
+    assert solve(mf.headmix_desc(torch.bfloat16, 64, [0], 1, 0, 6, 1, 1)) == mf.MF_ERR_UNSUPPORTED
