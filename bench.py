@@ -52,6 +52,8 @@ def parse():
                     help="only time whole-sequence compression against cached prefix + suffix + splice")
     ap.add_argument("--fetch-overlap", action="store_true",
                     help="only time a cache fetch overlapped with a stand-in for the receiver's early layers")
+    ap.add_argument("--headmix-fit", action="store_true",
+                    help="only time the least-squares head-mix fit at 8K over 16 layers")
     ap.add_argument("--several-receivers", action="store_true",
                     help="only time the 32K one-sender / two-receiver fused step three ways")
     return ap.parse_args()
@@ -216,6 +218,79 @@ def fetch_overlap_bench(reps: int, tau: float):
                       "results": out}))
 
 
+def headmix_fit_bench(reps: int, tau: float):
+    """8K, 16 layers: fit W[24 x 32] per layer by least squares from the
+    sender's compressed maps and a receiver's own (receiver-shaped Q/K, 24
+    heads, compressed at the same tau).  The Gram kernel is bound by fp64
+    FMA throughput: it takes every product of the padded head tile, and the
+    useful ones are those of heads that keep the block."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(3)
+    L, B = wl.num_layers, wl.B
+    lay = synth.batch_layout(wl)
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, B)
+
+    def compressed(w):
+        ins = [synth.layer_inputs(w, l, layout=lay) for l in range(L)]
+        q = torch.stack([x.q for x in ins]).to(dev)
+        k = torch.stack([x.k for x in ins]).to(dev)
+        del ins
+        cap = pipeline.count_capacity(batch, q, k, B, tau)
+        return pipeline.compress(pipeline.alloc_sender(batch, q, k, B, cap), q, k, tau)
+
+    sender = compressed(wl)
+    receiver = compressed(wl.replace(workload_id=32, H_s=wl.H_r))
+    H_s, H_r, R = wl.H_s, wl.H_r, batch.total_rowblocks
+    lmap = list(range(L))
+    desc = mf.headmix_desc(sender.values.dtype, B, lmap, L, H_s, H_r, sender.col_idx.numel(), receiver.col_idx.numel())
+    G = torch.empty((L, H_s, H_s), dtype=torch.float64, device=dev)
+    b = torch.empty((L, H_r, H_s), dtype=torch.float64, device=dev)
+    W = torch.empty((L, H_r, H_s), dtype=torch.float32, device=dev)
+    ws = torch.empty(mf.headmix_workspace_size(desc, batch), dtype=torch.uint8, device=dev)
+
+    def gram():
+        mf.headmix_gram(desc, batch, sender.row_ptr, sender.col_idx, sender.values, receiver.row_ptr,
+                        receiver.col_idx, receiver.values, G, b, ws)
+
+    def solve():
+        mf.headmix_solve(desc, G, b, 0.0, W)
+
+    gram(); solve()
+    torch.cuda.synchronize()
+    t_gram, t_solve = _event_ms(gram, reps), _event_ms(solve, reps)
+
+    # work: union blocks per (layer, row-block), heads keeping each
+    def keys(st, H):
+        rp = st.row_ptr.cpu().numpy().astype(np.int64)
+        rows = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+        l, i = rows // (H * R), rows % R
+        return (l * R + i) * batch.max_colblocks + st.col_idx[: st.nnz].cpu().numpy().astype(np.int64)
+    sk, s_cnt = np.unique(keys(sender, H_s), return_counts=True)
+    rk = keys(receiver, H_r)
+    r_cnt = np.zeros_like(s_cnt)
+    pos = np.searchsorted(sk, rk)
+    hit = (pos < len(sk)) & (sk[np.minimum(pos, len(sk) - 1)] == rk)
+    np.add.at(r_cnt, pos[hit], 1)
+    union = len(sk)
+    NA = H_s + H_r
+    executed = 2.0 * union * NA * H_s * B * B
+    useful = 2.0 * B * B * float(np.sum(s_cnt.astype(np.float64) ** 2 + r_cnt * s_cnt))
+    fp64_peak = 78.6
+    print(json.dumps({"metric": "least-squares head-mix fit from compressed maps",
+                      "config": {"workload": "bf16 causal 8192 tokens, 16 layers; sender 32 heads, receiver 24 heads "
+                                             "(own synthetic Q/K), B=64, both compressed at tau",
+                                 "tau": tau, "sender_kept_blocks": sender.nnz, "receiver_kept_blocks": receiver.nnz,
+                                 "union_blocks": union},
+                      "gram_ms": round(t_gram, 3), "solve_ms": round(t_solve, 3),
+                      "gram_executed_tflops": round(executed / t_gram / 1e9, 2),
+                      "gram_useful_tflops": round(useful / t_gram / 1e9, 2),
+                      "fp64_peak_tflops": fp64_peak,
+                      "gram_executed_frac": round(executed / t_gram / 1e9 / fp64_peak, 4)}))
+
+
 def several_receivers_bench(reps: int):
     """32K, one 40-head sender, receivers of 32 and 24 heads: one launch per
     receiver on one stream, on two streams, and one launch for both."""
@@ -338,6 +413,9 @@ def main():
         return
     if args.fetch_overlap:
         fetch_overlap_bench(max(args.steps, 3), args.tau)
+        return
+    if args.headmix_fit:
+        headmix_fit_bench(max(args.steps, 3), args.tau)
         return
     if args.several_receivers:
         several_receivers_bench(max(args.steps, 3))

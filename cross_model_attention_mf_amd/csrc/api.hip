@@ -411,6 +411,8 @@ mf_status mf_headmix_gram(const mf_headmix_desc* desc, const mf_batch* batch, co
       return fail(MF_ERR_INVALID, "%s: sender col_idx or values is NULL", fn);
     if (desc->receiver_capacity > 0 && (!r_col_idx || !r_values))
       return fail(MF_ERR_INVALID, "%s: receiver col_idx or values is NULL", fn);
+    if ((uintptr_t)s_values % 16 || (uintptr_t)r_values % 16)
+      return fail(MF_ERR_INVALID, "%s: values must be 16-byte aligned", fn);
     if ((int64_t)desc->sender_layers * desc->H_s * R > INT32_MAX - 1 || (int64_t)desc->num_layers * desc->H_r * R > INT32_MAX - 1)
       return fail(MF_ERR_UNSUPPORTED, "%s: too many CSR rows", fn);
   }

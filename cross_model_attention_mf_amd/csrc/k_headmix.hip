@@ -11,7 +11,9 @@
 // merges the sender heads' sorted column lists (lane h walks head h) and
 // moves each receiver head's list (lane r) up to the union block; the kept
 // blocks of every sender and receiver head are then staged through LDS, 64
-// entries at a time, transposed to [entry][head] in fp32, and each thread
+// entries at a time (16-byte loads of the next 64 in flight while the current
+// ones are multiplied; two LDS buffers, one barrier per step), transposed to
+// [entry][head] in fp32, and each thread
 // accumulates an 8 x 4 tile of [sender + receiver heads] x [sender heads]
 // products in fp64 (bf16 and fp32 products are exact in fp64).  Threads left
 // over split the entries and are summed in a fixed order; each workgroup
@@ -34,8 +36,42 @@ constexpr int kHmThreads = 256;
 constexpr int kHmChunk = 64;   // block entries staged per step
 constexpr int kNoCol = 0x7FFFFFFF;
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+constexpr int kHmItems = 4;   // staging items per thread: up to (64 + 64) heads x 8 parts / 256 threads
+
+// eight consecutive block entries, as loaded (16 bytes of bf16, 32 of fp32)
+template <typename T> struct Raw8;
+template <> struct Raw8<__hip_bfloat16> { uint4 w; };
+template <> struct Raw8<float> { uint4 w[2]; };
+
+__device__ __forceinline__ Raw8<__hip_bfloat16> load8(const __hip_bfloat16* p) {
+  return Raw8<__hip_bfloat16>{*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ Raw8<float> load8(const float* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  return Raw8<float>{{q[0], q[1]}};
+}
+__device__ __forceinline__ void unpack8(const Raw8<__hip_bfloat16>& r, float* x) {
+  const unsigned w[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float* x) {
+  const unsigned w[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
+}
+
+// A copy of a lane value the compiler cannot see through, so address math
+// derived from it is redone in place each step instead of being hoisted out of
+// the loop and held in registers.
+__device__ __forceinline__ int opaque(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
 
 struct HmTile {
   int T, KS;   // tiles, entry slices
@@ -46,20 +82,21 @@ __host__ __device__ inline HmTile hm_tiles(int NA, int Hs) {
   HmTile t;
   t.CT = (Hs + 3) / 4;
   t.T = ((NA + 7) / 8) * t.CT;
-  t.KS = t.T >= kHmThreads ? 1 : kHmThreads / t.T;
+  t.KS = 1;   // entry slices: the largest power of two with KS * T <= threads (divides the chunk)
+  while (2 * t.KS * t.T <= kHmThreads && 2 * t.KS <= kHmChunk) t.KS *= 2;
   return t;
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a) {
+__global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int NA = a.Hs + a.Hr;
   const int NAP = (NA + 7) / 8 * 8;                   // staged heads per entry (padded)
-  float* stage = reinterpret_cast<float*>(smem);      // [kHmChunk][NAP]
+  float* stage = reinterpret_cast<float*>(smem);      // 2 x [kHmChunk][NAP]
   double* red = reinterpret_cast<double*>(smem);      // reduction (reuses the stage)
   __shared__ int j_sh;
   __shared__ unsigned long long smask_sh, rmask_sh;
-  __shared__ long long svidx[64], rvidx[64];
+  __shared__ int svidx[64], rvidx[64];
 
   const int R = a.b.total_rb;
   const int l = blockIdx.x / R, i = blockIdx.x % R;
@@ -80,19 +117,19 @@ __global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a)
     for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
 
   // merge state (wave 0): sender list of head `lane`, receiver list of head `lane`
-  long long sp = 0, se = 0, rp = 0, re = 0;
+  int sp = 0, se = 0, rp = 0, re = 0;   // CSR entries (int32 row_ptr)
   int scol = kNoCol, rcol = kNoCol;
   if (wave == 0) {
     if (lane < a.Hs) {
       const size_t row = ((size_t)s * a.Hs + lane) * R + i;
-      sp = min((long long)a.s_row_ptr[row], (long long)a.s_cap);
-      se = min((long long)a.s_row_ptr[row + 1], (long long)a.s_cap);
+      sp = (int)min((long long)a.s_row_ptr[row], (long long)a.s_cap);
+      se = (int)min((long long)a.s_row_ptr[row + 1], (long long)a.s_cap);
       if (sp < se) scol = a.s_col[sp];
     }
     if (lane < a.Hr) {
       const size_t row = ((size_t)l * a.Hr + lane) * R + i;
-      rp = min((long long)a.r_row_ptr[row], (long long)a.r_cap);
-      re = min((long long)a.r_row_ptr[row + 1], (long long)a.r_cap);
+      rp = (int)min((long long)a.r_row_ptr[row], (long long)a.r_cap);
+      re = (int)min((long long)a.r_row_ptr[row + 1], (long long)a.r_cap);
       if (rp < re) rcol = a.r_col[rp];
     }
   }
@@ -131,42 +168,67 @@ __global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a)
     __syncthreads();
     if (j_sh == kNoCol) break;
     const unsigned long long sm = smask_sh, rm = rmask_sh;
-    for (int k0 = 0; k0 < BB; k0 += kHmChunk) {
-      // stage entries k0 .. k0 + 63 of every head's block (0 for heads that
-      // do not keep it), consecutive threads on consecutive heads
-      for (int idx = tid; idx < NAP * (kHmChunk / 8); idx += kHmThreads) {
-        const int slot = idx % NAP, part = idx / NAP;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const T* src = nullptr;
+    // this thread's staging items: (head slot, 8-entry part); the 16-byte
+    // loads of chunk c + 1 are in flight while chunk c is multiplied
+    const T* isrc[kHmItems];
+#pragma unroll
+    for (int t = 0; t < kHmItems; ++t) {
+      const int idx = tid + t * kHmThreads;
+      const int slot = idx % NAP, part = idx / NAP;
+      const T* src = nullptr;
+      if (part < kHmChunk / 8) {
         if (slot < a.Hs) {
-          if ((sm >> slot) & 1ull) src = sval + (size_t)svidx[slot] * BB;
+          if ((sm >> slot) & 1ull) src = sval + (size_t)svidx[slot] * BB + 8 * part;
         } else if (slot < NA) {
           const int r = slot - a.Hs;
-          if ((rm >> r) & 1ull) src = rval + (size_t)rvidx[r] * BB;
+          if ((rm >> r) & 1ull) src = rval + (size_t)rvidx[r] * BB + 8 * part;
         }
-        if (src) {
+      }
+      isrc[t] = src;
+    }
+    Raw8<T> pre[kHmItems];
+    auto load = [&](int k0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = to_f32(src[k0 + 8 * part + e]);
+      for (int t = 0; t < kHmItems; ++t) pre[t] = isrc[t] ? load8(isrc[t] + k0) : Raw8<T>{};
+    };
+    load(0);
+    const int nch = BB / kHmChunk;
+    for (int c = 0; c < nch; ++c) {
+      float* st = stage + (size_t)(c & 1) * kHmChunk * NAP;
+#pragma unroll
+      for (int t = 0; t < kHmItems; ++t) {
+        const int idx = opaque(tid + t * kHmThreads);
+        const int slot = idx % NAP, part = idx / NAP;
+        if (part < kHmChunk / 8) {
+          float x[8];
+          unpack8(pre[t], x);
+          float* q = st + 8 * part * NAP + slot;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e * NAP] = x[e];
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) stage[(8 * part + e) * NAP + slot] = x[e];
       }
       __syncthreads();
+      if (c + 1 < nch) load((c + 1) * kHmChunk);
       if (active) {
-        for (int k = ks; k < kHmChunk; k += tl.KS) {
-          const float* row = stage + k * NAP;
-          double xc[4], xr[8];
+        const int nk = kHmChunk / tl.KS;   // uniform trip count
+#pragma unroll 1
+        for (int it = 0; it < nk; ++it) {
+          const float* row = st + (ks + it * tl.KS) * NAP;
+          const float4 cv = *reinterpret_cast<const float4*>(row + c0);
+          const double xc[4] = {(double)cv.x, (double)cv.y, (double)cv.z, (double)cv.w};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) xc[v] = (double)row[c0 + v];
+          for (int h = 0; h < 2; ++h) {
+            const float4 rv = *reinterpret_cast<const float4*>(row + a0 + 4 * h);
+            const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-          for (int u = 0; u < 8; ++u) xr[u] = (double)row[a0 + u];
+            for (int u = 0; u < 4; ++u) {
+              const double xr = (double)r4[u];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = fma(xr[u], xc[v], acc[u][v]);
+              for (int v = 0; v < 4; ++v) acc[4 * h + u][v] = fma(xr, xc[v], acc[4 * h + u][v]);
+            }
+          }
         }
       }
-      __syncthreads();
     }
   }
 
@@ -282,7 +344,7 @@ size_t headmix_partial_bytes(int L, int total_rb, int Hs, int Hr) {
 size_t headmix_gram_lds_bytes(int Hs, int Hr) {
   const int NA = Hs + Hr, NAP = (NA + 7) / 8 * 8;
   const HmTile tl = hm_tiles(NA, Hs);
-  const size_t st = (size_t)kHmChunk * NAP * sizeof(float);
+  const size_t st = (size_t)2 * kHmChunk * NAP * sizeof(float);
   const size_t rd = tl.KS > 1 ? (size_t)tl.T * 32 * sizeof(double) : 0;
   return st > rd ? st : rd;
 }

@@ -294,7 +294,8 @@ size_t mf_headmix_workspace_size(const mf_headmix_desc* desc, const mf_batch* ba
  *   gram   DEVICE fp64 [num_layers][H_s][H_s], overwritten
  *   cross  DEVICE fp64 [num_layers][H_r][H_s]: cross[l][r][h] = b_r[h]
  *   workspace  DEVICE, at least mf_headmix_workspace_size() bytes
- * Both CSRs must use the same B and dtype. */
+ * Both CSRs must use the same B and dtype; both values arrays must be 16-byte
+ * aligned (MF_ERR_INVALID otherwise). */
 mf_status mf_headmix_gram(const mf_headmix_desc* desc, const mf_batch* batch,
                           const int32_t* s_row_ptr, const int32_t* s_col_idx, const void* s_values,
                           const int32_t* r_row_ptr, const int32_t* r_col_idx, const void* r_values,

@@ -308,6 +308,8 @@ def test_headmix_validation_paths():
     assert gram(mf.headmix_desc(torch.bfloat16, 64, [0], 1, 8, 6, -1, 1)) == mf.MF_ERR_INVALID
     assert gram(mf.headmix_desc(torch.bfloat16, 32, [0], 1, 8, 6, 1, 1)) == mf.MF_ERR_INVALID  # batch planned for 64
     assert gram(good, ws_bytes=need - 1) == mf.MF_ERR_WORKSPACE
+    assert L.mf_headmix_gram(ctypes.byref(good), ctypes.byref(bc), fake, fake, fake + 8, fake, fake, fake,
+                             fake, fake, fake, need, None) == mf.MF_ERR_INVALID   # misaligned values
     assert gram(good, gram_ptr=None) == mf.MF_ERR_INVALID
     assert "gram" in L.mf_last_error_message().decode()
     # no layers: nothing to do
