@@ -11,12 +11,12 @@
 // merges the sender heads' sorted column lists (lane h walks head h) and
 // moves each receiver head's list (lane r) up to the union block; the kept
 // blocks of every sender and receiver head are then staged through LDS, 64
-// entries at a time (16-byte loads of the next 64 in flight while the current
+// entries at a time (16-byte loads of the next 128 in flight while the current
 // ones are multiplied; two LDS buffers, one barrier per step), transposed to
-// [entry][head] in fp32, and each thread
-// accumulates an 8 x 4 tile of [sender + receiver heads] x [sender heads]
-// products in fp64 (bf16 and fp32 products are exact in fp64).  Threads left
-// over split the entries and are summed in a fixed order; each workgroup
+// [entry][head] in fp32.  The products are a dense contraction over the
+// entries, [sender + receiver heads] x [sender heads], on fp64 MFMA
+// (16 x 16 x 4; bf16 and fp32 values are exact in fp64, and so are their
+// products), 16 x 16 output tiles dealt to the four waves.  Each workgroup
 // writes its partial products, and headmix_reduce_kernel adds them over the
 // row-blocks in order, so results do not depend on scheduling.
 // headmix_solve_kernel: one workgroup per layer, Cholesky of G + lambda I in
@@ -73,27 +73,27 @@ __device__ __forceinline__ int opaque(int x) {
   return y;
 }
 
-struct HmTile {
-  int T, KS;   // tiles, entry slices
-  int CT;      // column tiles
-};
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-__host__ __device__ inline HmTile hm_tiles(int NA, int Hs) {
-  HmTile t;
-  t.CT = (Hs + 3) / 4;
-  t.T = ((NA + 7) / 8) * t.CT;
-  t.KS = 1;   // entry slices: the largest power of two with KS * T <= threads (divides the chunk)
-  while (2 * t.KS * t.T <= kHmThreads && 2 * t.KS <= kHmChunk) t.KS *= 2;
-  return t;
+constexpr int kHmMaxTiles = 8;   // 16 x 16 output tiles per wave: (128 / 16) x (64 / 16) / 4 waves
+
+// heads staged per entry (sender then receiver, padded to whole 16-row
+// tiles) and the LDS pitch of one entry: the first count >= that which is 16
+// mod 32, so the 4 entries one MFMA operand read touches (16 consecutive
+// heads each) fall on 4 disjoint quarters of the 64 banks
+__host__ __device__ inline int hm_rows(int Hs, int Hr) { return (Hs + Hr + 15) / 16 * 16; }
+__host__ __device__ inline int hm_pitch(int Hs, int Hr) {
+  const int r = hm_rows(Hs, Hr);
+  return r % 32 == 16 ? r : r + 16;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs a) {
+template <typename T, int MT>
+__global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int NA = a.Hs + a.Hr;
-  const int NAP = (NA + 7) / 8 * 8;                   // staged heads per entry (padded)
-  float* stage = reinterpret_cast<float*>(smem);      // 2 x [kHmChunk][NAP]
-  double* red = reinterpret_cast<double*>(smem);      // reduction (reuses the stage)
+  const int NAP = hm_rows(a.Hs, a.Hr);                 // staged heads per entry
+  const int P = hm_pitch(a.Hs, a.Hr);                  // floats per staged entry
+  float* stage = reinterpret_cast<float*>(smem);      // 2 x [kHmChunk][P]
   __shared__ int j_sh;
   __shared__ unsigned long long smask_sh, rmask_sh;
   __shared__ int svidx[64], rvidx[64];
@@ -102,19 +102,16 @@ __global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs
   const int l = blockIdx.x / R, i = blockIdx.x % R;
   const int s = a.layer_map[l];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const HmTile tl = hm_tiles(NA, a.Hs);
-  const bool active = tid < tl.T * tl.KS;
-  const int tile = tid % tl.T, ks = tid / tl.T;
-  const int a0 = 8 * (tile / tl.CT), c0 = 4 * (tile % tl.CT);
+  // output tiles: 16 x 16 blocks of [staged heads] x [sender heads]; wave w
+  // takes tiles w, w + 4, ...
+  const int CT = (a.Hs + 15) / 16, T16 = (NAP / 16) * CT;
   const int BB = a.B * a.B;
   const T* __restrict__ sval = reinterpret_cast<const T*>(a.s_val);
   const T* __restrict__ rval = reinterpret_cast<const T*>(a.r_val);
 
-  double acc[8][4];
+  f64x4 acc[MT];   // this wave's tiles (MT >= its tile count)
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+  for (int m = 0; m < MT; ++m) acc[m] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // merge state (wave 0): sender list of head `lane`, receiver list of head `lane`
   int sp = 0, se = 0, rp = 0, re = 0;   // CSR entries (int32 row_ptr)
@@ -174,7 +171,7 @@ __global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs
 #pragma unroll
     for (int t = 0; t < kHmItems; ++t) {
       const int idx = tid + t * kHmThreads;
-      const int slot = idx % NAP, part = idx / NAP;
+      const int slot = idx % NAP, part = idx / NAP;   // consecutive lanes, consecutive heads
       const T* src = nullptr;
       if (part < kHmChunk / 8) {
         if (slot < a.Hs) {
@@ -186,15 +183,16 @@ __global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs
       }
       isrc[t] = src;
     }
-    Raw8<T> pre[kHmItems];
-    auto load = [&](int k0) {
+    // two chunks of loads in flight: chunk c + 2 is issued into the registers
+    // chunk c was just staged from
+    Raw8<T> preA[kHmItems], preB[kHmItems];
+    auto load = [&](Raw8<T>* pre, int k0) {
 #pragma unroll
       for (int t = 0; t < kHmItems; ++t) pre[t] = isrc[t] ? load8(isrc[t] + k0) : Raw8<T>{};
     };
-    load(0);
-    const int nch = BB / kHmChunk;
-    for (int c = 0; c < nch; ++c) {
-      float* st = stage + (size_t)(c & 1) * kHmChunk * NAP;
+    const int nch = BB / kHmChunk;   // even: B * B / 64 for B in {32, 64, 128}
+    auto step = [&](Raw8<T>* pre, int c) {
+      float* st = stage + (size_t)(c & 1) * kHmChunk * P;
 #pragma unroll
       for (int t = 0; t < kHmItems; ++t) {
         const int idx = opaque(tid + t * kHmThreads);
@@ -202,61 +200,55 @@ __global__ void __launch_bounds__(kHmThreads, 2) headmix_gram_kernel(HeadmixArgs
         if (part < kHmChunk / 8) {
           float x[8];
           unpack8(pre[t], x);
-          float* q = st + 8 * part * NAP + slot;
+          float* q = st + 8 * part * P + slot;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e * NAP] = x[e];
+          for (int e = 0; e < 8; ++e) q[e * P] = x[e];
         }
       }
       __syncthreads();
-      if (c + 1 < nch) load((c + 1) * kHmChunk);
-      if (active) {
-        const int nk = kHmChunk / tl.KS;   // uniform trip count
-#pragma unroll 1
-        for (int it = 0; it < nk; ++it) {
-          const float* row = st + (ks + it * tl.KS) * NAP;
-          const float4 cv = *reinterpret_cast<const float4*>(row + c0);
-          const double xc[4] = {(double)cv.x, (double)cv.y, (double)cv.z, (double)cv.w};
+      if (c + 2 < nch) load(pre, (c + 2) * kHmChunk);
+      // MFMA 16x16x4 fp64: lane L supplies A[L % 16][L / 16] (head 16 ra +
+      // L % 16, entry 4 kk + L / 16) and B[L / 16][L % 16] (sender head
+      // 16 cb + L % 16, same entry)
+      const float* col = st + (lane >> 4) * P + (lane & 15);
+#pragma unroll 2
+      for (int kk = 0; kk < kHmChunk / 4; ++kk) {
+        const float* rowk = col + 4 * kk * P;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float4 rv = *reinterpret_cast<const float4*>(row + a0 + 4 * h);
-            const float r4[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const double xr = (double)r4[u];
-#pragma unroll
-              for (int v = 0; v < 4; ++v) acc[4 * h + u][v] = fma(xr, xc[v], acc[4 * h + u][v]);
-            }
+        for (int m = 0; m < MT; ++m) {
+          const int t = wave + 4 * m;
+          if (t < T16) {
+            const int ra = t / CT, cb = t % CT;
+            const double av = (double)rowk[16 * ra];
+            const double bv = (double)rowk[16 * cb];
+            acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[m], 0, 0, 0);
           }
         }
       }
+    };
+    load(preA, 0);
+    load(preB, kHmChunk);
+    for (int c = 0; c < nch; c += 2) {
+      step(preA, c);
+      step(preB, c + 1);
     }
   }
 
-  // sum the entry slices in a fixed order (slice KS - 1 down to 0), then write
-  // this row-block's partial products
-  for (int sl = tl.KS - 1; sl >= 1; --sl) {
-    if (active && ks == sl) {
+  // this row-block's partial products: element j of lane L is row 4 j + L / 16,
+  // column L % 16 of its tile (the fp64 MFMA's output layout)
+  double* out = a.partial + (size_t)blockIdx.x * NA * a.Hs;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+  for (int m = 0; m < MT; ++m) {
+    const int t = wave + 4 * m;
+    if (t < T16) {
+      const int ra = t / CT, cb = t % CT;
+      const int cc = 16 * cb + (lane & 15);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[(size_t)tile * 32 + u * 4 + v] = acc[u][v];
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * ra + 4 * j + (lane >> 4);
+        if (rr < NA && cc < a.Hs) out[(size_t)rr * a.Hs + cc] = acc[m][j];
+      }
     }
-    __syncthreads();
-    if (active && ks == sl - 1) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] += red[(size_t)tile * 32 + u * 4 + v];
-    }
-    __syncthreads();
-  }
-  if (active && ks == 0) {
-    double* out = a.partial + (size_t)blockIdx.x * NA * a.Hs;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (a0 + u < NA && c0 + v < a.Hs) out[(size_t)(a0 + u) * a.Hs + c0 + v] = acc[u][v];
   }
 }
 
@@ -342,11 +334,7 @@ size_t headmix_partial_bytes(int L, int total_rb, int Hs, int Hr) {
 }
 
 size_t headmix_gram_lds_bytes(int Hs, int Hr) {
-  const int NA = Hs + Hr, NAP = (NA + 7) / 8 * 8;
-  const HmTile tl = hm_tiles(NA, Hs);
-  const size_t st = (size_t)2 * kHmChunk * NAP * sizeof(float);
-  const size_t rd = tl.KS > 1 ? (size_t)tl.T * 32 * sizeof(double) : 0;
-  return st > rd ? st : rd;
+  return (size_t)2 * kHmChunk * hm_pitch(Hs, Hr) * sizeof(float);
 }
 
 int launch_headmix_gram(const HeadmixArgs& a, mf_dtype dt, double* gram, double* cross, void* stream) {
@@ -355,7 +343,14 @@ int launch_headmix_gram(const HeadmixArgs& a, mf_dtype dt, double* gram, double*
   if (a.L == 0) return 0;
   if (a.b.total_rb > 0) {
     const size_t lds = headmix_gram_lds_bytes(a.Hs, a.Hr);
-    auto kern = dt == MF_BF16 ? headmix_gram_kernel<__hip_bfloat16> : headmix_gram_kernel<float>;
+    const int tiles = (hm_rows(a.Hs, a.Hr) / 16) * ((a.Hs + 15) / 16);
+    const int per_wave = (tiles + 3) / 4;
+    const bool bf = dt == MF_BF16;
+    auto kern = per_wave <= 1 ? (bf ? headmix_gram_kernel<__hip_bfloat16, 1> : headmix_gram_kernel<float, 1>)
+              : per_wave <= 2 ? (bf ? headmix_gram_kernel<__hip_bfloat16, 2> : headmix_gram_kernel<float, 2>)
+              : per_wave <= 4 ? (bf ? headmix_gram_kernel<__hip_bfloat16, 4> : headmix_gram_kernel<float, 4>)
+                              : (bf ? headmix_gram_kernel<__hip_bfloat16, kHmMaxTiles>
+                                    : headmix_gram_kernel<float, kHmMaxTiles>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.L * a.b.total_rb)), dim3(kHmThreads), lds, s, a);
