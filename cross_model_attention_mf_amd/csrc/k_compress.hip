@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
   const size_t row = lh * a.b.total_rb + rb;
   const int64_t base = a.row_ptr[row];
   const int hk = h / (a.H / a.Hkv);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qh = w & 1, kh = w >> 1;
 
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
     }
   }
   __syncthreads();
-  const int n = nkept;
+  const int n = __builtin_amdgcn_readfirstlane(nkept);
   if (n == 0) return;
 
   const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)l * a.lsk +
@@ -470,7 +470,7 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
   const size_t kstride = (size_t)a.Hkv * D;
   const int klast = ri.klen - 1;
   auto issue = [&](int t) {
-    const int j = jlist[t < n ? t : n - 1];
+    const int j = __builtin_amdgcn_readfirstlane(jlist[t < n ? t : n - 1]);
     char* stage = ring + (t % XNST) * STAGE;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {

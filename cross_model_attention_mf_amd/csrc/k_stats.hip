@@ -270,7 +270,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
   extern __shared__ __align__(16) char smem[];
   __shared__ int item_sh;
 
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int xcd = blockIdx.x % kXcds;
   const int ngroups = hdr[kXcds];
@@ -285,7 +285,9 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
   for (;;) {
     if (threadIdx.x == 0) item_sh = atomicAdd(&hdr[xcd], 1);
     __syncthreads();
-    const long long item = item_sh;
+    // wave-uniform: every lane read the same word (readfirstlane lets the
+    // compiler keep the item's addresses and block offsets in scalar registers)
+    const long long item = __builtin_amdgcn_readfirstlane(item_sh);
     __syncthreads();
     if (item >= nitems) break;
     const long long p = xcd + (long long)kXcds * (item / ngroups);
