@@ -40,8 +40,8 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -221,9 +221,9 @@ def fetch_overlap_bench(reps: int, tau: float):
 def headmix_fit_bench(reps: int, tau: float):
     """8K, 16 layers: fit W[24 x 32] per layer by least squares from the
     sender's compressed maps and a receiver's own (receiver-shaped Q/K, 24
-    heads, compressed at the same tau).  The Gram kernel is bound by fp64
-    FMA throughput: it takes every product of the padded head tile, and the
-    useful ones are those of heads that keep the block."""
+    heads, compressed at the same tau).  The Gram kernel runs on fp64 MFMA
+    over 16 x 16 tiles of [sender + receiver heads] x [sender heads] (padded
+    to 16); the useful products are those of heads that keep the block."""
     import torch
     from cross_model_attention_mf_amd import mapflow as mf
     from cross_model_attention_mf_amd import pipeline, synth
@@ -275,8 +275,8 @@ def headmix_fit_bench(reps: int, tau: float):
     hit = (pos < len(sk)) & (sk[np.minimum(pos, len(sk) - 1)] == rk)
     np.add.at(r_cnt, pos[hit], 1)
     union = len(sk)
-    NA = H_s + H_r
-    executed = 2.0 * union * NA * H_s * B * B
+    rows, cols = -(-(H_s + H_r) // 16) * 16, -(-H_s // 16) * 16
+    executed = 2.0 * union * rows * cols * B * B
     useful = 2.0 * B * B * float(np.sum(s_cnt.astype(np.float64) ** 2 + r_cnt * s_cnt))
     fp64_peak = 78.6
     print(json.dumps({"metric": "least-squares head-mix fit from compressed maps",
@@ -475,9 +475,15 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_stats = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_comp = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    t_map = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    d_stats = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    d_comp = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    d_map = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    d_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    t_stats, t_comp, t_map = d_stats.mean() * 1e-3, d_comp.mean() * 1e-3, d_map.mean() * 1e-3
+
+    def spread(d):
+        return {"median": round(float(np.median(d)), 4), "p10": round(float(np.percentile(d, 10)), 4),
+                "p90": round(float(np.percentile(d, 90)), 4)}
     ms_per_step = wall / args.steps * 1e3
     assert int(st.row_ptr[-1]) == cap
 
@@ -526,12 +532,28 @@ def main():
                            "us_per_layer": round((t_stats + t_comp) / L * 1e6, 1),
                            "stats_us_per_layer": round(t_stats / L * 1e6, 1),
                            "select_extract_us_per_layer": round(t_comp / L * 1e6, 1)},
+        # per-launch durations in ms (HIP events on the launch stream); one
+        # step's working set (about 15 GB) is far beyond the 256 MB Infinity
+        # Cache, so consecutive steps do not run warm
+        "timing_ms": {"step": spread(d_step), "block_stats": spread(d_stats),
+                      "select_scan_extract": spread(d_comp), "mapped_attn_v": spread(d_map)},
         "kept_blocks": cap,
         "kept_fraction": round(cap / (L * wl.H_s * sum(i + 1 for i in range(batch.total_rowblocks))), 4),
         "roofline": {k_: v_ for k_, v_ in rooflines[dominant].items() if k_ != "us_per_launch"},
         "roofline_kernel": dominant,
         "rooflines": rooflines,
     }
+    # union of the sender heads' kept sets per (layer, row-block): its size
+    # against the causal blocks, and how many heads keep each union block
+    rp_h = st.row_ptr.cpu().numpy().astype(np.int64)
+    rows = np.repeat(np.arange(len(rp_h) - 1), np.diff(rp_h))
+    R = batch.total_rowblocks
+    ukeys = ((rows // (wl.H_s * R)) * R + rows % R) * batch.max_colblocks + \
+        st.col_idx[:cap].cpu().numpy().astype(np.int64)
+    union = int(np.unique(ukeys).size)
+    res["union_blocks"] = union
+    res["union_density"] = round(union / (L * sum(i + 1 for i in range(R))), 4)
+    res["head_overlap"] = round(cap / (wl.H_s * union), 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, tau, min(args.cpu_sample_layers, L))
