@@ -20,14 +20,23 @@
  *                       head, form the learned linear head combination on
  *                       chip, multiply by the receiver's own V and accumulate
  *                       the output, with no dense receiver map (paragraph
- *                       "第三").
+ *                       "第三"); mf_mapped_attn_v_multi serves several
+ *                       receivers of one compressed map in one launch.
+ *
+ * Around it: a prefix cache of compressed maps (mf_prefix_block_hashes,
+ * mf_map_cache_*; paragraph "第二"), and the offline least-squares fit of the
+ * head mapping W from compressed maps (mf_headmix_*; section "从内部表示…").
  *
  * Conventions shared by every entry point
  *   - Pointers marked DEVICE are GPU memory, HOST are CPU memory.  The caller
- *     owns and allocates every buffer; the library allocates nothing.
+ *     owns and allocates every device buffer; the library allocates no device
+ *     memory.  The prefix cache keeps its index in host memory and a small
+ *     pinned host buffer for its copy tables.
  *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = default
- *     stream).  The only blocking call is mf_compress_blocks with a non-NULL
- *     nnz_out, which synchronises `stream` once to read the kept-block count.
+ *     stream).  mf_compress_blocks with a non-NULL nnz_out synchronises
+ *     `stream` once to read the kept-block count; a prefix-cache insert or
+ *     splice waits on the host only until the previous such call's small
+ *     table copies have left the pinned buffer.
  *   - Every argument is validated on the host before anything is launched;
  *     a failing call returns a status other than MF_OK, launches nothing and
  *     records a message for mf_last_error_message().  No exceptions or aborts
