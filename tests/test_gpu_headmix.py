@@ -168,3 +168,16 @@ def test_repeat_calls_are_bit_identical():
     b = pipeline.fit_headmix(s, r, [0], 0.0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("H_s,H_r", [(40, 24), (64, 64), (1, 1)])
+def test_fit_with_wide_and_single_heads(H_s, H_r):
+    """Several 16 x 16 output tiles per wave (up to 8 for 64 + 64 heads) and
+    the one-head extreme."""
+    seqlens = (5 * 32 + 7, 40)
+    sw = synth.Workload(name="hm_wide_s", workload_id=48, dtype="bf16", H_s=H_s, H_r=4, d=64, B=32,
+                        taus=(0.9,), seqlens=seqlens, num_layers=1, w_var=0.5)
+    rw = sw.replace(workload_id=49, H_s=H_r)
+    sender = compress(sw, 0.9, [0])
+    receiver = compress(rw, 0.9, [0])
+    check_fit(sender, receiver, [0], 1e-4)
