@@ -371,23 +371,40 @@ def cpu_baseline(wl, tau, n_layers):
     lay = synth.batch_layout(wl)
     rbs = orc.enumerate_rowblocks(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
     scale = orc.default_scale(wl.d)
-    dt = 0.0
+    # the oracle's own steps for one (row-block, head) unit, in its order, each
+    # timed: softmax + block masses (statistics), selection + extraction, and
+    # the mapped output of the row-block
+    t_stats = t_sel = t_map = 0.0
     for layer in range(n_layers):
         li = synth.layer_inputs(wl, layer, layout=lay)
         q, k, v = synth.to_f64(li.q), synth.to_f64(li.k), synth.to_f64(li.v)
         W = li.w.double().numpy()
-        t0 = time.perf_counter()
         for rb in rbs:
             kv = []
             for h in range(wl.H_s):
-                u = orc.compress_unit(q, k, rb, h, wl.B, tau, scale)
-                kv.append((u.sel.kept, u.values))
+                t0 = time.perf_counter()
+                qr = q[rb.q0: rb.q0 + rb.rows, h, :]
+                kk = k[rb.k0: rb.k0 + rb.klen, orc.kv_head(h, q.shape[1], k.shape[1]), :]
+                ncand = orc.num_candidates(rb, wl.B)
+                P, _ = orc.causal_probs(qr, kk[: min(rb.klen, ncand * wl.B)], rb.pos0 + np.arange(rb.rows), scale)
+                m = orc.block_masses(P, wl.B, ncand)
+                t1 = time.perf_counter()
+                sel = orc.select_blocks(m, tau)
+                kv.append((sel.kept, orc.extract_blocks(P, sel.kept, wl.B)))
+                t2 = time.perf_counter()
+                t_stats += t1 - t0
+                t_sel += t2 - t1
+            t0 = time.perf_counter()
             orc.mapped_rowblock(kv, W, v, rb, wl.B)
-        dt += time.perf_counter() - t0
-    step_s = dt / n_layers * wl.num_layers
+            t_map += time.perf_counter() - t0
+    dt = t_stats + t_sel + t_map
+    per_step = wl.num_layers / n_layers
     threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
-    return {"value": round(lay.total_q / step_s, 3), "unit": "tokens/s", "cores": int(threads),
+    rate = lambda t: round(lay.total_q / (t * per_step), 3)
+    return {"value": rate(dt), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
+            "stages_tokens_per_s": {"block_stats": rate(t_stats), "select_extract": rate(t_sel),
+                                    "mapped_attn_v": rate(t_map)},
             "sample": f"layers 0..{n_layers - 1}: all {len(rbs)} row-blocks x all {wl.H_s} sender heads "
                       f"(stats, selection, extraction, mapped output); {dt:.1f} s measured, "
                       f"scaled by layer count to {wl.num_layers} layers"}
