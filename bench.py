@@ -560,6 +560,23 @@ def main():
         "roofline_kernel": dominant,
         "rooflines": rooflines,
     }
+    # a plain 1 GiB device copy as the practical HBM ceiling (read + write
+    # bytes over the copy's time), beside the 8 TB/s published peak
+    src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_c = torch.empty_like(src_c)
+    for _ in range(2):
+        dst_c.copy_(src_c)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(5):
+        dst_c.copy_(src_c)
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del src_c, dst_c
+    res["hbm_copy_GB_per_s"] = round(copy_gbs, 1)
+    res["mapped_attn_v"]["copy_frac"] = round(map_gbs / copy_gbs, 4)
     # union of the sender heads' kept sets per (layer, row-block): its size
     # against the causal blocks, and how many heads keep each union block
     rp_h = st.row_ptr.cpu().numpy().astype(np.int64)
