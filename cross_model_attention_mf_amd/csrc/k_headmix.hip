@@ -82,16 +82,21 @@ constexpr int kHmMaxTiles = 8;   // 16 x 16 output tiles per wave: (128 / 16) x 
 // mod 32, so the 4 entries one MFMA operand read touches (16 consecutive
 // heads each) fall on 4 disjoint quarters of the 64 banks
 __host__ __device__ inline int hm_rows(int Hs, int Hr) { return (Hs + Hr + 15) / 16 * 16; }
-__host__ __device__ inline int hm_pitch(int Hs, int Hr) {
-  const int r = hm_rows(Hs, Hr);
-  return r % 32 == 16 ? r : r + 16;
+// staged heads per entry as a power of two (>= hm_rows), so the staging index
+// splits into (head, part) with a mask and a shift
+__host__ __device__ inline int hm_slots_log2(int Hs, int Hr) {
+  int lg = 4;
+  while ((1 << lg) < hm_rows(Hs, Hr)) ++lg;
+  return lg;
 }
+__host__ __device__ inline int hm_pitch(int Hs, int Hr) { return (1 << hm_slots_log2(Hs, Hr)) + 16; }
 
 template <typename T, int MT>
 __global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int NA = a.Hs + a.Hr;
-  const int NAP = hm_rows(a.Hs, a.Hr);                 // staged heads per entry
+  const int NAP = hm_rows(a.Hs, a.Hr);                 // heads in whole 16-row tiles
+  const int SL = hm_slots_log2(a.Hs, a.Hr);            // staged heads per entry: 1 << SL
   const int P = hm_pitch(a.Hs, a.Hr);                  // floats per staged entry
   float* stage = reinterpret_cast<float*>(smem);      // 2 x [kHmChunk][P]
   __shared__ int j_sh;
@@ -171,7 +176,7 @@ __global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a)
 #pragma unroll
     for (int t = 0; t < kHmItems; ++t) {
       const int idx = tid + t * kHmThreads;
-      const int slot = idx % NAP, part = idx / NAP;   // consecutive lanes, consecutive heads
+      const int slot = idx & ((1 << SL) - 1), part = idx >> SL;   // consecutive lanes, consecutive heads
       const T* src = nullptr;
       if (part < kHmChunk / 8) {
         if (slot < a.Hs) {
@@ -196,7 +201,7 @@ __global__ void __launch_bounds__(kHmThreads) headmix_gram_kernel(HeadmixArgs a)
 #pragma unroll
       for (int t = 0; t < kHmItems; ++t) {
         const int idx = opaque(tid + t * kHmThreads);
-        const int slot = idx % NAP, part = idx / NAP;
+        const int slot = idx & ((1 << SL) - 1), part = idx >> SL;
         if (part < kHmChunk / 8) {
           float x[8];
           unpack8(pre[t], x);
