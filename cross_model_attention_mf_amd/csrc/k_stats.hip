@@ -361,6 +361,9 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
     }
 
     float m_ref[2] = {0.f, 0.f}, m_run[2] = {0.f, 0.f};
+    // (m_run - m_ref) c2 in log2 units, rounded once from fp64; it changes
+    // only when a block overflows the reference
+    float eoff[2] = {0.f, 0.f};
     double l_run[2] = {1.0, 1.0};
 
     for (int t = 0; t <= jtop; ++t) {
@@ -443,6 +446,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
             const float mx = block_max(qt);
             const float s = block_sum(qt, mx * c2);
             m_ref[qt] = m_run[qt] = mx;
+            eoff[qt] = 0.f;
             l_run[qt] = (double)s;
             evq[qt] = __builtin_amdgcn_logf(s);
           }
@@ -462,13 +466,14 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
               const float m_new = fmaxf(m_run[qt], block_max(qt));
               l_run[qt] *= (double)__builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
               m_run[qt] = m_new;
+              eoff[qt] = (float)(((double)m_new - (double)m_ref[qt]) * c2d);
               s[qt] = block_sum(qt, m_new * c2);
             }
           }
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
             l_run[qt] += (double)s[qt];
-            evq[qt] = __builtin_amdgcn_logf(s[qt]) + (float)(((double)m_run[qt] - (double)m_ref[qt]) * c2d);
+            evq[qt] = __builtin_amdgcn_logf(s[qt]) + eoff[qt];
           }
         }
         ev = hi ? evq[1] : evq[0];
