@@ -54,6 +54,8 @@ def parse():
                     help="only time a cache fetch overlapped with a stand-in for the receiver's early layers")
     ap.add_argument("--headmix-fit", action="store_true",
                     help="only time the least-squares head-mix fit at 8K over 16 layers")
+    ap.add_argument("--varlen", action="store_true",
+                    help="only time every chunk step of the varlen / chunked / paged workload")
     ap.add_argument("--several-receivers", action="store_true",
                     help="only time the 32K one-sender / two-receiver fused step three ways")
     return ap.parse_args()
@@ -291,6 +293,60 @@ def headmix_fit_bench(reps: int, tau: float):
                       "gram_executed_frac": round(executed / t_gram / 1e9 / fp64_peak, 4)}))
 
 
+def varlen_bench(reps: int):
+    """32 packed sequences (lognormal lengths), prefill chunks of 2048 query
+    rows over the whole prefix, paged V (16-token pages): every chunk step of
+    the prefill, each one batch of the whole path.  Layers are independent
+    work; 4 of the workload's 16 are timed, because generating the synthetic
+    inputs on the host dominates the run."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(4).replace(num_layers=4)
+    L = wl.num_layers
+    steps = []
+    tot_q = 0
+    for step in range(synth.num_chunk_steps(wl)):
+        lay = synth.batch_layout(wl, step)
+        ins = [synth.layer_inputs(wl, l, step, lay) for l in range(L)]
+        q = torch.stack([x.q for x in ins]).to(dev)
+        k = torch.stack([x.k for x in ins]).to(dev)
+        W = torch.stack([x.w for x in ins]).to(dev)
+        pvs = [synth.page_values(x.v, lay, wl.page_size, synth.page_rng(wl, 0)) for x in ins]
+        pool = torch.stack([pv.pool for pv in pvs]).to(dev)
+        bt = torch.from_numpy(pvs[0].block_table).to(dev)
+        del ins, pvs
+        batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, lay.q_pos0, wl.B)
+        cap = pipeline.count_capacity(batch, q, k, wl.B, wl.tau)
+        st = pipeline.alloc_sender(batch, q, k, wl.B, cap)
+        out = torch.empty((L, lay.total_q, wl.H_r, wl.d), dtype=torch.bfloat16, device=dev)
+        desc = mf.receiver_desc(pool, wl.H_s, wl.H_r, wl.d, wl.B, list(range(L)), L, out[0].numel(),
+                                st.col_idx.numel(), bt, wl.page_size)
+        steps.append((batch, q, k, st, cap, desc, W, pool, out))
+        tot_q += lay.total_q
+        print(f"[bench] chunk step {step}: {lay.total_q} query rows, {cap} kept blocks", file=sys.stderr, flush=True)
+
+    def one(b):
+        batch, q, k, st, cap, desc, W, pool, out = b
+        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass, st.stats_workspace)
+        mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, wl.tau, st.row_ptr, st.col_idx,
+                           st.values, cap, st.workspace, sync_count=False)
+        mf.mapped_attn_v(desc, batch, st.row_ptr, st.col_idx, st.values, W, pool, out)
+
+    def all_steps():
+        for b in steps:
+            one(b)
+
+    ms = _event_ms(all_steps, reps)
+    print(json.dumps({"metric": "whole path over every prefill chunk step, varlen / chunked / paged",
+                      "config": {"workload": "bf16, 32 sequences lognormal(7.5, 0.8) lengths in [256, 16384], "
+                                             "chunks of 2048 query rows, 16-token pages, 32 -> 24 heads, d=128, B=64",
+                                 "layers_timed": L, "tau": wl.tau, "chunk_steps": len(steps),
+                                 "query_rows": tot_q, "kept_blocks": int(sum(b[4] for b in steps))},
+                      "ms_all_steps": round(ms, 3), "tokens_per_s": round(tot_q / (ms * 1e-3), 1)}))
+
+
 def several_receivers_bench(reps: int):
     """32K, one 40-head sender, receivers of 32 and 24 heads: one launch per
     receiver on one stream, on two streams, and one launch for both."""
@@ -433,6 +489,9 @@ def main():
         return
     if args.headmix_fit:
         headmix_fit_bench(max(args.steps, 3), args.tau)
+        return
+    if args.varlen:
+        varlen_bench(max(args.steps, 3))
         return
     if args.several_receivers:
         several_receivers_bench(max(args.steps, 3))
