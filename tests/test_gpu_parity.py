@@ -240,3 +240,23 @@ def test_wave_and_workgroup_selection_agree(monkeypatch, B, seqlens):
         assert torch.equal(a.state.row_ptr, b.state.row_ptr)
         assert torch.equal(a.state.col_idx, b.state.col_idx)
         assert torch.equal(a.state.values, b.state.values)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_portable_and_mfma_extraction_agree_with_oracle(monkeypatch, d):
+    """bf16, B = 64: the MFMA extraction and its portable twin write the same
+    CSR; their values (each rounded to bf16 from its own fp32 scores) agree to
+    a bf16 rounding step, and both match the oracle."""
+    wl = tiny_structured("bf16", workload_id=17, B=64, d=d, H_s=6, H_r=4,
+                         seqlens=(64 * 5 + 9, 64 * 2, 33), chunk=None)
+    runs = []
+    for portable in ("1", "0"):
+        monkeypatch.setenv("MF_PORTABLE_EXTRACT", portable)
+        run = parity.run_gpu(wl, 0.9, [0])
+        parity.check_layer(run, 0)
+        runs.append(run.state)
+    a, b = runs
+    assert a.nnz == b.nnz
+    assert torch.equal(a.row_ptr, b.row_ptr) and torch.equal(a.col_idx, b.col_idx)
+    diff = (a.values[: a.nnz].float() - b.values[: b.nnz].float()).abs().max().item()
+    assert diff <= 2.0 ** -8, diff
