@@ -51,10 +51,11 @@
  *   - Supported shapes: B in {32, 64, 128}; d in {64, 128}; 1 <= H <= 64 with
  *     H_kv dividing H; dtype fp32 or bf16; chunk starts multiple of B; keys
  *     of a sequence per call <= MF_MAX_KEYS.
- *   - Thread safety: calls on distinct streams may run concurrently; the
- *     compressed CSR is read-only for mf_mapped_attn_v, so any number of
- *     receivers may read one sender state at once (paragraph "第二": one
- *     sender state serves several downstream models).
+ *   - Thread safety: calls on distinct streams may run concurrently, except
+ *     calls that share a workspace or a prefix cache; the compressed CSR is
+ *     read-only for mf_mapped_attn_v, so any number of receivers may read one
+ *     sender state at once (paragraph "第二": one sender state serves several
+ *     downstream models).  Error messages are kept per host thread.
  */
 #ifndef MAPFLOW_H
 #define MAPFLOW_H
