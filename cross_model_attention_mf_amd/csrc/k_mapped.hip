@@ -113,26 +113,36 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 //   group):  C_e[(g, r)][q] += sum_h [g == g2] W[r][h] P_h[32cb + 8 g2 + e][q]
 //   so lane (g, q) holds, for e = 0..7, the mixed map A_r[q][32cb + 8g + e]:
 //   exactly the A operand (8 keys per lane group) of the P.V MFMA, and the
-//   mixed map never leaves registers.  Key groups not yet mixed are still
-//   zero, so P.V runs twice per step, after stages 1 and 3, each time over
-//   the 16 keys whose V rows are in LDS:
+//   mixed map never leaves registers.
 //   P.V (MFMA 16x16x32, K = keys): O_r[q][n] += A_r[q][c] V_r[c][n].
 //
-// Memory pipeline: key-major block rows (RQ contiguous queries) are copied
-// HBM -> LDS with global_load_lds (16 bytes per lane, no registers) into a
-// 3-slot ring (2 when the sender heads leave LDS for only two): the copies
-// of stage s + 2 are issued at stage s, right after the barrier that opens
-// it, so two stages are in flight while one is mixed.
-// The V rows of a 16-key half arrive in their own buffer, issued at the
-// half's first stage and used after its second; they are staged once per
+// Two memory pipelines; key-major block rows (RQ contiguous queries) are
+// copied HBM -> LDS with global_load_lds (16 bytes per lane, no registers).
+//
+// Half-stage ring (when the sender heads, padded to a multiple of 16, leave
+// room for five 4-key slots beside a 32-key V buffer): stage s mixes the
+// half-stages 2s and 2s+1 and, right after the barrier that opens it, issues
+// 2s+3 and 2s+4 into the slots stage s-1 consumed, so one and a half stages
+// are in flight.  A slot holds 4 key rows per head, unpadded; odd heads hold
+// each key pair swapped, so a transpose read of one key meets neighbouring
+// heads in opposite bank halves.  One copy covers a pair of heads.  The V
+// rows of a 32-key step arrive at its first stage, and P.V runs once per
+// step, after stage 3, over all 32 keys.
+//
+// Stage ring (other shapes): a 3-slot ring of 8-key stages (2 when the
+// sender heads leave LDS for only two), each head's rows padded by 128 bytes:
+// the copies of stage s + 2 are issued at stage s.  Key groups not yet mixed
+// are still zero, so P.V runs twice per step, after stages 1 and 3, each
+// time over the 16 keys whose V rows are in LDS.  The V rows of a 16-key
+// half arrive in their own buffer, issued at the half's first stage and used
+// after its second (or one half ahead with two buffers).  V rows are staged once per
 // value head the group's receiver heads read (grouped-query receivers share
 // them), not once per receiver head.  Only sender heads that keep the block
 // issue P copies; the slot of an absent head keeps finite values from an
 // earlier block (or the initial zeros), which meet a zero weight.  Every
 // stage issues its P copies last, so one counted wait at the top of each
-// stage (vmcnt = the wave's P copies of the previous stage, a wave-uniform
-// count; 0 with a 2-slot ring) covers both the stage's P rows and the
-// half's V rows.  The copies are issued as inline
+// stage (vmcnt = the wave's newest P copies, a wave-uniform count; 0 with a
+// 2-slot ring) covers the rows the stage reads and the V rows of its step.  The copies are issued as inline
 // assembly, which the compiler does not track, so it inserts no drain of the
 // ring before LDS accesses; the kernel's own waits and barriers order them.
 // The column lists of the sender heads and the page ids of paged values also
@@ -249,6 +259,18 @@ struct MapCfg {
   static constexpr int RPI = 1024 / VROW;              // V rows per copy instruction
   static_assert(HPAD % NW == 0, "P copies must split evenly over the waves");
   static_assert(16 % RPI == 0, "a value head's 16 rows fill whole copy instructions");
+  // half-stage ring: NHS slots of 4 key rows per head, unpadded, beside a
+  // V buffer of 32 keys (P.V then covers 32 live keys)
+  static constexpr int NHS = 5;
+  static constexpr int HSB = HPAD * 4 * PROW;          // one half-slot
+  static constexpr int VB32 = KVC * 32 * VROW;
+  static constexpr bool HALF = (HPAD / 2) % NW == 0 && (size_t)NHS * HSB + (size_t)VB32 + kMapMeta <= 163840;
+  static constexpr int PWH = HPAD / 2 / NW;            // head-pair copies per wave per half-stage
+  static constexpr int HPU = B / 4;                    // half-stages per block
+  static constexpr int RING = HALF ? NHS * HSB : NSLOT * SBYTES;
+  static constexpr int VK = HALF ? 32 : 16;            // keys per V buffer
+  static constexpr int VBUF = HALF ? VB32 : VB;
+  static constexpr int VTOT = HALF ? VB32 : VBYTES;
 };
 
 // value heads one group of 8 receiver heads reads, at most over the groups
@@ -273,6 +295,8 @@ size_t mapped_mfma_lds_bytes(int B, int D, int Hs, int kvc) {
   const size_t nvb = fits(nslot, 2) ? 2 : 1;
   const size_t obytes = (size_t)64 * 8 * D * 2;       // output staging (aliases the ring and V)
   size_t main = nslot * stage + nvb * vb;
+  const size_t hsb = hpad * 4 * 128, vb32 = (size_t)kvc * 32 * D * 2;
+  if (hpad % 16 == 0 && 5 * hsb + vb32 + kMapMeta <= 163840) main = 5 * hsb + vb32;
   if (obytes > main) main = obytes;
   return main + kMapMeta;
 }
@@ -288,8 +312,8 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   constexpr int hpad = C::HPAD;
   extern __shared__ __align__(16) char smem[];
   char* ring = smem;
-  char* Vs = smem + C::NSLOT * C::SBYTES;
-  size_t main_bytes = C::NSLOT * C::SBYTES + C::VBYTES;
+  char* Vs = smem + C::RING;
+  size_t main_bytes = C::RING + C::VTOT;
   if ((size_t)C::RQ * 8 * D * 2 > main_bytes) main_bytes = (size_t)C::RQ * 8 * D * 2;
   UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + main_bytes);
   int* curcol = reinterpret_cast<int*>(UI + 2);        // next column of each sender head
@@ -411,6 +435,38 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         async_copy16(pbase[i] + (size_t)si * 8 * B, buf + (size_t)(wave + i * C::NW) * C::HSTR);
     return __builtin_popcount(plive);
   };
+  // Half-stage copies: instruction (wave, i) copies head pair c = wave + i NW,
+  // lane L head 2c + L / 32, row r = (L / 8) % 4, chunk L % 8.  Row r of
+  // head h holds key r ^ (h & 1) of the half-stage (odd heads swap key
+  // pairs, which puts the same key of neighbouring heads in opposite bank
+  // halves), chunk from source chunk (L % 8) ^ swz_p(h).  A pair issues a
+  // copy when either head keeps the block; the lanes of a head that does not
+  // read the block's first rows at offset 0 of the values (finite, and met
+  // by a zero weight).
+  const bf16* hbase[C::HALF ? C::PWH : 1];
+  unsigned hlive = 0;
+  auto prep_h = [&](const UnionInfo* ui) {
+    const unsigned long long mk = ui ? ui->mask : 0ull;
+    const int r = (lane >> 3) & 3, pc = lane & 7;
+    unsigned bits = 0;
+#pragma unroll
+    for (int i = 0; i < C::PWH; ++i) {
+      const int c = wave + i * C::NW, h = 2 * c + (lane >> 5);
+      const int sc = pc ^ swz_p(h);
+      const bool live = h < a.Hs && ((mk >> h) & 1ull);
+      const bool plv = ((mk >> (2 * c)) & 3ull) != 0ull && 2 * c < a.Hs;
+      hbase[i] = vals + (live ? (size_t)ui->vidx[h] * B * B : (size_t)0) + (size_t)(r ^ (h & 1)) * B + qoff + 8 * sc;
+      bits |= plv ? 1u << i : 0u;
+    }
+    hlive = __builtin_amdgcn_readfirstlane(bits);
+  };
+  auto issue_h = [&](int hsi, char* slot) {
+#pragma unroll
+    for (int i = 0; i < C::PWH; ++i)
+      if ((hlive >> i) & 1u)
+        async_copy16(hbase[i] + (size_t)hsi * 4 * B, slot + (size_t)(wave + i * C::NW) * 1024);
+    return __builtin_popcount(hlive);
+  };
   // The group's receiver heads read nkv consecutive value heads kv0 ..
   // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
   // V rows of 16-key half hh of the block, staged once per value head ->
@@ -420,14 +476,14 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
   auto issue_v = [&](const UnionInfo* ui, int hh, int buf) {
     const int ln = opaque(lane);
-    const int ninst = nkv * (16 / C::RPI);
-    char* vdst = Vs + (size_t)buf * C::VB;
+    const int ninst = nkv * (C::VK / C::RPI);
+    char* vdst = Vs + (size_t)buf * C::VBUF;
 #pragma unroll 1
     for (int k = wave; k < ninst; k += C::NW) {
       const int rho = k * C::RPI + ln / C::VCPR;
       const int p = ln % C::VCPR;
-      const int kvl = rho >> 4, cl = rho & 15;
-      const int kl = 16 * hh + cl;                     // key inside the block
+      const int kvl = rho / C::VK, cl = rho % C::VK;
+      const int kl = C::VK * hh + cl;                  // key inside the block
       const int key = ui->j * B + kl;
       const bool live = key < ri.klen;
       const int g = kv0 + kvl;
@@ -462,9 +518,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int h = 32 * hk + 8 * lg + (lr >> 2) + 4 * t;
-      moff[hk][t] = (unsigned)(h * C::HSTR + ((pch ^ swz_p(h)) << 4) + pwithin);
+      moff[hk][t] = (unsigned)(h * (C::HALF ? 4 * C::PROW : C::HSTR) + ((pch ^ swz_p(h)) << 4) + pwithin);
     }
   const float* wrow = Wsh + (4 * hq + (lr & 3)) * 64;
+  const unsigned ppar = ((lr >> 2) & 1) * C::PROW;     // this lane's heads are odd: key pairs swapped
 
   if (UI[0].j != 0x7FFFFFFF) {
     // stages are numbered over the whole walk: stage s is stage s % SPU of
@@ -477,10 +534,16 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     // previous stage's P copies, always its last, may be.  With a 2-slot
     // ring everything is waited for.
     int ops_prev = 0, p_prev = 0;
-    prep_p(&UI[0]);
-    if (C::NVB == 2) issue_v(&UI[0], 0, 0);
+    if constexpr (C::HALF) {
+      prep_h(&UI[0]);
 #pragma unroll
-    for (int t = 0; t < C::AHEAD; ++t) p_prev = issue_p(t, ring + (size_t)t * C::SBYTES);
+      for (int t = 0; t < 3; ++t) p_prev = issue_h(t, ring + (size_t)t * C::HSB);
+    } else {
+      prep_p(&UI[0]);
+      if (C::NVB == 2) issue_v(&UI[0], 0, 0);
+#pragma unroll
+      for (int t = 0; t < C::AHEAD; ++t) p_prev = issue_p(t, ring + (size_t)t * C::SBYTES);
+    }
     ops_prev = p_prev;
     bf16x8 Wk[2];
     f32x4 Cacc[8];
@@ -490,7 +553,11 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       // P rows of stage s and the V rows of its half have landed (only the
       // P copies issued at stage s - 1, the wave's latest, may still be in
       // flight)
-      if (C::AHEAD == 1) {
+      if (C::HALF) {
+        // half-stages 2s and 2s+1 have landed; only 2s+2, issued last at
+        // stage s-1, may be in flight
+        wait_vmcnt_upto<C::PWH>(p_prev);
+      } else if (C::AHEAD == 1) {
         wait_vmcnt<0>();
       } else if (C::NVB == 1) {
         wait_vmcnt_upto<C::PW>(p_prev);
@@ -518,7 +585,10 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       // V rows: with two buffers, those of the next half at the last stage of
       // this one (into the other buffer); with one, those of this half at
       // its first stage
-      if (C::NVB == 2) {
+      if (C::HALF) {
+        // V rows of this 32-key step, needed at its last stage
+        if (g2 == 0) ops += issue_v(ui, si >> 2, 0);
+      } else if (C::NVB == 2) {
         if (g2 & 1) {
           const int s1 = s + 1;
           const UnionInfo* ui1 = &UI[(s1 / C::SPU) & 1];
@@ -530,7 +600,19 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         ops += issue_v(ui, si >> 1, 0);
       }
       // ---- P copies of stage s + AHEAD (dummy rows past the last block)
-      {
+      if constexpr (C::HALF) {
+        // half-stages 2s+3 and 2s+4, into the slots stage s-1 consumed
+#pragma unroll
+        for (int k = 3; k <= 4; ++k) {
+          const int t = 2 * s + k, u2 = t / C::HPU, hsi = t % C::HPU;
+          if (hsi == 0) {
+            const UnionInfo* ui2 = &UI[u2 & 1];
+            prep_h(ui2->j != 0x7FFFFFFF ? ui2 : nullptr);
+          }
+          p_prev = issue_h(hsi, ring + (size_t)(t % C::NHS) * C::HSB);
+          ops += p_prev;
+        }
+      } else {
         const int s2 = s + C::AHEAD, u2 = s2 / C::SPU, si2 = s2 % C::SPU;
         if (si2 == 0) {
           const UnionInfo* ui2 = &UI[u2 & 1];
@@ -544,6 +626,8 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       // ---- head mix over the 8 keys of key group g2: lanes of key group g2
       // take W, the others zero (block-diagonal)
       const char* cur = ring + (size_t)(s % C::NSLOT) * C::SBYTES;
+      const char* curA = ring + (size_t)((2 * s) % C::NHS) * C::HSB;
+      const char* curB = ring + (size_t)((2 * s + 1) % C::NHS) * C::HSB;
       const bf16x8 zero8 = {};
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
@@ -560,8 +644,17 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
           bf16x8 pop[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const bf16x4 lo = tr_read(cur, o0 + e * C::PROW);
-            const bf16x4 hi = tr_read(cur, o1 + e * C::PROW);
+            bf16x4 lo, hi;
+            if constexpr (C::HALF) {
+              const char* hs = e < 4 ? curA : curB;
+              const int ep = e & 3;
+              const unsigned kofs = (ep & 1) ? (ep - 1) * C::PROW + (C::PROW - ppar) : ep * C::PROW + ppar;
+              lo = tr_read(hs, o0 + kofs);
+              hi = tr_read(hs, o1 + kofs);
+            } else {
+              lo = tr_read(cur, o0 + e * C::PROW);
+              hi = tr_read(cur, o1 + e * C::PROW);
+            }
             const bf16x8 pv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             pop[e] = hv ? pv : zero8;
           }
@@ -570,7 +663,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
             Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop[e], Cacc[e], 0, 0, 0);
         }
       }
-      if (g2 & 1) {
+      if (C::HALF ? g2 == 3 : (g2 & 1) != 0) {
         // ---- P.V over the 16 keys of this half: A_r[q][32cb + 8lg + e] =
         // Cacc[e][i]; lane groups of the other half hold zeros, and their V
         // rows (any finite row of the buffer) add nothing
@@ -580,13 +673,13 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
           for (int ee = 0; ee < 8; ++ee) Aop[i][ee] = (bf16)Cacc[ee][i];
         const int nlo = 4 * (lr & 3);
-        const char* Vh = Vs + (size_t)(C::NVB == 2 ? (s >> 1) & 1 : 0) * C::VB;
+        const char* Vh = Vs + (size_t)(!C::HALF && C::NVB == 2 ? (s >> 1) & 1 : 0) * C::VBUF;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // value head of receiver 8 grp + 4 hq + i, local to the group (a
           // padding receiver past Hr reads some staged row: its mixed map is 0)
           const int kvl = min((8 * grp + 4 * hq + i) / ratio - kv0, KVC - 1);
-          const int rho0 = kvl * 16 + 8 * (lg & 1) + (lr >> 2);
+          const int rho0 = kvl * C::VK + 8 * (C::HALF ? lg : (lg & 1)) + (lr >> 2);
           const int sw0 = swz_v(rho0, C::VCPR);         // same for rho0 + 4
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) {
