@@ -58,6 +58,10 @@ def parse():
                     help="only time every chunk step of the varlen / chunked / paged workload")
     ap.add_argument("--several-receivers", action="store_true",
                     help="only time the 32K one-sender / two-receiver fused step three ways")
+    ap.add_argument("--pipelined", action="store_true",
+                    help="only time the 8K step over layer groups, the fused step of a group overlapping "
+                         "the next group's statistics on a second stream")
+    ap.add_argument("--groups", type=int, default=4, help="layer groups of --pipelined")
     return ap.parse_args()
 
 
@@ -396,6 +400,49 @@ def several_receivers_bench(reps: int):
                       "results": res}))
 
 
+def pipelined_bench(reps: int, tau: float, layers: int, groups: int):
+    """The 8K step over layer groups: each group's statistics and compression
+    on the current stream, its fused step on a second one, so the fused step
+    of group g overlaps the statistics of group g + 1.  Timed against the
+    same groups in order on one stream and against one group (the default
+    bench step); every schedule must give the same O bit for bit."""
+    import torch
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(3).replace(num_layers=layers)
+    lay = synth.batch_layout(wl)
+    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(layers)]
+    q = torch.stack([x.q for x in ins]).to(dev)
+    k = torch.stack([x.k for x in ins]).to(dev)
+    v = torch.stack([x.v for x in ins]).to(dev)
+    W = torch.stack([x.w for x in ins]).to(dev)
+    del ins
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    out = torch.empty((layers, lay.total_q, wl.H_r, wl.d), dtype=torch.bfloat16, device=dev)
+    ref, res = None, {}
+    for G in sorted({1, groups}):
+        pipe = pipeline.LayerGroupPipeline(batch, q, k, v, W, out, wl.B, tau, wl.H_r, G)
+        for overlap in ((False, True) if G > 1 else (False,)):
+            out.zero_()
+            pipe.step(overlap)
+            pipe.step(overlap)
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = out.clone()
+            ms = _event_ms(lambda: pipe.step(overlap), reps)
+            name = "one_group_in_order" if G == 1 else f"{G}_groups_" + ("pipelined" if overlap else "in_order")
+            res[name] = {"ms": round(ms, 3), "tokens_per_s": round(lay.total_q / (ms * 1e-3), 1),
+                         "same_as_one_group": bool(torch.equal(out, ref))}
+        del pipe
+        torch.cuda.synchronize()
+    print(json.dumps({"metric": "whole-path step over layer groups, fused step overlapped with the next group's statistics",
+                      "config": {"workload": f"bf16 causal 8192 tokens, {layers} mapped layers, sender 32 heads -> "
+                                             "receiver 24 heads, d=128, B=64, structured Q/K",
+                                 "tau": tau, "groups": groups, "timed_steps": reps},
+                      "results": res}))
+
+
 def source_hash(rel: str) -> str:
     with open(os.path.join(ROOT, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -495,6 +542,9 @@ def main():
         return
     if args.several_receivers:
         several_receivers_bench(max(args.steps, 3))
+        return
+    if args.pipelined:
+        pipelined_bench(max(args.steps, 3), args.tau, args.layers, args.groups)
         return
 
     if args.copy_calibration:

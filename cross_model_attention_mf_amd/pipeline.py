@@ -148,6 +148,59 @@ def fetch_overlapped(cache: mf.MapCache, keys, m: int, n_blocks: int, suffix: Op
     return nnz
 
 
+class LayerGroupPipeline:
+    """The whole path over groups of layers, with the fused step of group g
+    on a second stream while block statistics and compression of group g + 1
+    run on the current one.  Receiver layer l reads sender layer l.
+
+    Each group owns its compressed state; the kept-block capacity of every
+    group is counted once at construction (a host sync), so a step issues
+    none.  The kernels and their inputs are those of the sequential order,
+    so the outputs are the same bit for bit; only the overlap changes.  The
+    statistics kernel is bound by MFMA and VALU work, the fused kernel by its
+    copy pipeline, so the two share the chip better than either alone."""
+
+    def __init__(self, batch: mf.Batch, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 W: torch.Tensor, out: torch.Tensor, B: int, tau: float, H_r: int, groups: int,
+                 map_stream: Optional[torch.cuda.Stream] = None):
+        L = q.shape[0]
+        if not 1 <= groups <= L:
+            raise ValueError(f"groups must lie in [1, {L}], got {groups}")
+        self.batch, self.tau = batch, tau
+        self.map_stream = map_stream if map_stream is not None else torch.cuda.Stream()
+        self.groups = []
+        for g in range(groups):
+            l0, l1 = g * L // groups, (g + 1) * L // groups
+            qg, kg = q[l0:l1], k[l0:l1]
+            cap = count_capacity(batch, qg, kg, B, tau)
+            st = alloc_sender(batch, qg, kg, B, cap)
+            og = out[l0:l1]
+            desc = mf.receiver_desc(v[l0:l1], st.desc.H_s, H_r, st.desc.d, B, list(range(l1 - l0)), l1 - l0,
+                                    og[0].numel(), st.col_idx.numel())
+            self.groups.append((qg, kg, cap, st, desc, W[l0:l1], v[l0:l1], og))
+
+    @property
+    def capacity(self) -> int:
+        return sum(g[2] for g in self.groups)
+
+    def step(self, pipelined: bool = True) -> None:
+        cur = torch.cuda.current_stream()
+        # the previous step's fused launches read the states this step rewrites
+        cur.wait_stream(self.map_stream)
+        for qg, kg, cap, st, desc, Wg, vg, og in self.groups:
+            mf.block_stats(st.desc, self.batch, qg, kg, st.row_lse, st.block_mass, st.stats_workspace, cur)
+            mf.compress_blocks(st.desc, self.batch, qg, kg, st.row_lse, st.block_mass, self.tau, st.row_ptr,
+                               st.col_idx, st.values, cap, st.workspace, sync_count=False, stream=cur)
+            if pipelined:
+                self.map_stream.wait_stream(cur)
+                mf.mapped_attn_v(desc, self.batch, st.row_ptr, st.col_idx, st.values, Wg, vg, og,
+                                 stream=self.map_stream)
+            else:
+                mf.mapped_attn_v(desc, self.batch, st.row_ptr, st.col_idx, st.values, Wg, vg, og, stream=cur)
+        if pipelined:
+            cur.wait_stream(self.map_stream)
+
+
 def fit_headmix(sender: SenderState, receiver: SenderState, layer_map: Sequence[int], lam: float = 0.0,
                 stream=None):
     """Least-squares head mix from a sender's and a receiver's compressed maps

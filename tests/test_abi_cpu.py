@@ -322,3 +322,12 @@ def test_headmix_validation_paths():
     assert solve(good, lam=float("nan")) == mf.MF_ERR_INVALID
     assert solve(good, W=None) == mf.MF_ERR_INVALID
     assert solve(mf.headmix_desc(torch.bfloat16, 64, [0], 1, 0, 6, 1, 1)) == mf.MF_ERR_UNSUPPORTED
+
+
+def test_layer_group_pipeline_rejects_bad_group_counts():
+    import torch
+    from cross_model_attention_mf_amd import pipeline
+    q = torch.zeros((4, 8, 2, 64), dtype=torch.bfloat16)
+    for g in (0, 5):
+        with pytest.raises(ValueError):
+            pipeline.LayerGroupPipeline(None, q, q, q, None, None, 64, 0.9, 2, g)

@@ -262,3 +262,28 @@ def test_portable_and_mfma_extraction_agree_with_oracle(monkeypatch, d):
     assert torch.equal(a.row_ptr, b.row_ptr) and torch.equal(a.col_idx, b.col_idx)
     diff = (a.values[: a.nnz].float() - b.values[: b.nnz].float()).abs().max().item()
     assert diff <= 2.0 ** -8, diff
+
+
+@pytest.mark.parametrize("groups", [2, 3])
+def test_layer_group_pipeline_equals_one_pass(groups):
+    # each layer group's fused step on a second stream, overlapping the next
+    # group's statistics: the same O bit for bit as one pass over all layers,
+    # which itself matches the oracle
+    wl = tiny_structured("bf16", workload_id=18, B=64, d=128, H_s=32, H_r=24, seqlens=(5 * 64 + 9,),
+                         num_layers=4)
+    run = parity.run_gpu(wl, 0.9, list(range(4)))
+    parity.check_layer(run, 3)
+    dev = torch.device("cuda")
+    q = torch.stack([x.q for x in run.inputs]).to(dev)
+    k = torch.stack([x.k for x in run.inputs]).to(dev)
+    v = torch.stack([x.v for x in run.inputs]).to(dev)
+    W = torch.stack([x.w for x in run.inputs]).to(dev)
+    batch = mf.Batch(run.layout.cu_seqlens_q, run.layout.cu_seqlens_k, None, wl.B)
+    out = torch.empty_like(run.outs[0])
+    pipe = pipeline.LayerGroupPipeline(batch, q, k, v, W, out, wl.B, 0.9, wl.H_r, groups)
+    assert pipe.capacity == run.state.nnz
+    for overlap in (True, False, True):
+        out.zero_()
+        pipe.step(overlap)
+        torch.cuda.synchronize()
+        assert torch.equal(out, run.outs[0])
