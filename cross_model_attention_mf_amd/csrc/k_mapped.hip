@@ -441,8 +441,8 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // pairs, which puts the same key of neighbouring heads in opposite bank
   // halves), chunk from source chunk (L % 8) ^ swz_p(h).  A pair issues a
   // copy when either head keeps the block; the lanes of a head that does not
-  // read the block's first rows at offset 0 of the values (finite, and met
-  // by a zero weight).
+  // keep it read rows of the first stored block instead (finite values that
+  // meet a zero weight).
   const bf16* hbase[C::HALF ? C::PWH : 1];
   unsigned hlive = 0;
   auto prep_h = [&](const UnionInfo* ui) {
@@ -469,8 +469,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   };
   // The group's receiver heads read nkv consecutive value heads kv0 ..
   // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
-  // V rows of 16-key half hh of the block, staged once per value head ->
-  // Vs, row 16 kvl + key
+  // V rows of the VK-key part hh of the block (16 keys with the stage ring,
+  // 32 with the half-stage ring), staged once per value head -> Vs, row
+  // VK kvl + key
   const int ratio = R.Hr / R.Hkv;
   const int kv0 = (8 * grp) / ratio;
   const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
@@ -525,14 +526,21 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 
   if (UI[0].j != 0x7FFFFFFF) {
     // stages are numbered over the whole walk: stage s is stage s % SPU of
-    // union block s / SPU; issue runs two stages ahead of the mix
-    // Copies outstanding at the top of a stage: with two V buffers every copy
-    // is needed two stages after the one that issued it at the earliest, so
-    // all of the previous stage's copies may still be in flight.  With one
-    // V buffer the V rows issued at a half's first stage (and the merge's
-    // copies, issued before them) are needed at its second, so only the
-    // previous stage's P copies, always its last, may be.  With a 2-slot
-    // ring everything is waited for.
+    // union block s / SPU (half-stage t is half-stage t % HPU of block
+    // t / HPU).  Copies outstanding at the top of a stage:
+    //  - half-stage ring: the prologue issues half-stages 0..2 and stage s
+    //    issues 2s+3 and 2s+4, so only 2s+2, the previous stage's last
+    //    copies, may still be in flight; the V rows of a step (and the
+    //    merge's copies), issued before the P copies of its first stage, have
+    //    landed by its second;
+    //  - stage ring, two V buffers: every copy is needed two stages after
+    //    the one that issued it at the earliest, so all of the previous
+    //    stage's copies may still be in flight;
+    //  - stage ring, one V buffer: the V rows issued at a half's first stage
+    //    (and the merge's copies, issued before them) are needed at its
+    //    second, so only the previous stage's P copies, always its last, may
+    //    be;
+    //  - 2-slot stage ring: everything is waited for.
     int ops_prev = 0, p_prev = 0;
     if constexpr (C::HALF) {
       prep_h(&UI[0]);
