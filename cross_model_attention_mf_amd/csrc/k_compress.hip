@@ -215,15 +215,30 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) carry_s = 0;
   __syncthreads();
+  // a thread's 32 counts are 128 contiguous bytes: whole chunks move as
+  // 16-byte vectors when both arrays are 16-byte aligned
+  const bool aligned = ((reinterpret_cast<uintptr_t>(a.counts) | reinterpret_cast<uintptr_t>(a.row_ptr)) & 15) == 0;
   for (int64_t base = 0; base < a.n; base += (int64_t)kScanThreads * kScanPer) {
     const int64_t i0 = base + (int64_t)tid * kScanPer;
+    const bool vec = aligned && i0 + kScanPer <= a.n;
     int32_t x[kScanPer];
     long long tot = 0;
+    if (vec) {
+      const int4* src = reinterpret_cast<const int4*>(a.counts + i0);
 #pragma unroll
-    for (int u = 0; u < kScanPer; ++u) {
-      x[u] = i0 + u < a.n ? a.counts[i0 + u] : 0;
-      tot += x[u];
+      for (int u = 0; u < kScanPer / 4; ++u) {
+        const int4 c = src[u];
+        x[4 * u] = c.x;
+        x[4 * u + 1] = c.y;
+        x[4 * u + 2] = c.z;
+        x[4 * u + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kScanPer; ++u) x[u] = i0 + u < a.n ? a.counts[i0 + u] : 0;
     }
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) tot += x[u];
     long long v = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -235,10 +250,27 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(ScanArgs a) {
     long long pre = carry_s;
     for (int u = 0; u < w; ++u) pre += wsum[u];
     long long run = pre + v - tot;
+    if (vec) {
+      int4* dst = reinterpret_cast<int4*>(a.row_ptr + i0);
 #pragma unroll
-    for (int u = 0; u < kScanPer; ++u) {
-      if (i0 + u < a.n) a.row_ptr[i0 + u] = (int32_t)run;
-      run += x[u];
+      for (int u = 0; u < kScanPer / 4; ++u) {
+        int4 o;
+        o.x = (int32_t)run;
+        run += x[4 * u];
+        o.y = (int32_t)run;
+        run += x[4 * u + 1];
+        o.z = (int32_t)run;
+        run += x[4 * u + 2];
+        o.w = (int32_t)run;
+        run += x[4 * u + 3];
+        dst[u] = o;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kScanPer; ++u) {
+        if (i0 + u < a.n) a.row_ptr[i0 + u] = (int32_t)run;
+        run += x[u];
+      }
     }
     __syncthreads();
     if (tid == kScanThreads - 1) carry_s = run;

@@ -287,3 +287,26 @@ def test_layer_group_pipeline_equals_one_pass(groups):
         pipe.step(overlap)
         torch.cuda.synchronize()
         assert torch.equal(out, run.outs[0])
+
+
+def test_compress_with_row_ptr_not_16_byte_aligned():
+    # a row_ptr that is only 4-byte aligned takes the scan's element-wise
+    # path: the same CSR as the vector path
+    wl = tiny_structured("bf16", workload_id=19, B=64, d=64, H_s=6, H_r=4, seqlens=(9 * 64 + 5, 300),
+                         num_layers=2)
+    run = parity.run_gpu(wl, 0.9, [0, 1])
+    parity.check_layer(run, 1)
+    st = run.state
+    dev = torch.device("cuda")
+    q = torch.stack([x.q for x in run.inputs]).to(dev)
+    k = torch.stack([x.k for x in run.inputs]).to(dev)
+    big = torch.full((st.row_ptr.numel() + 1,), -1, dtype=torch.int32, device=dev)
+    rp = big[1:]
+    assert rp.data_ptr() % 16 != 0
+    col = torch.empty_like(st.col_idx)
+    vals = torch.empty_like(st.values)
+    nnz = mf.compress_blocks(st.desc, st.batch, q, k, st.row_lse, st.block_mass, 0.9, rp, col, vals,
+                             col.numel(), st.workspace, sync_count=True)
+    assert nnz == st.nnz
+    assert torch.equal(rp, st.row_ptr)
+    assert torch.equal(col[:nnz], st.col_idx[:nnz]) and torch.equal(vals[:nnz], st.values[:nnz])
