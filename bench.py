@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_bf16_8k_16layers.json")
 KERNEL_SOURCES = {
     "stats_mfma_kernel": "cross_model_attention_mf_amd/csrc/k_stats.hip",
     "mapped_mfma_kernel": "cross_model_attention_mf_amd/csrc/k_mapped.hip",
@@ -63,6 +63,13 @@ def parse():
                          "the next group's statistics on a second stream")
     ap.add_argument("--groups", type=int, default=4, help="layer groups of --pipelined")
     return ap.parse_args()
+
+
+def _emit(rec: dict) -> None:
+    """Print one JSON record, naming the command that produced it."""
+    rec = dict(rec)
+    rec["command"] = " ".join(["python", "bench.py"] + sys.argv[1:])
+    print(json.dumps(rec), flush=True)
 
 
 def _event_ms(fn, reps: int) -> float:
@@ -137,10 +144,10 @@ def prefix_cache_bench(reps: int, tau: float):
         t_spl = float(np.median(ts))
         rows.append({"cached_rowblocks": m, "suffix_compress_ms": round(t_suf, 3), "splice_ms": round(t_spl, 3),
                      "total_ms": round(t_suf + t_spl, 3), "bit_exact": bool(same)})
-    print(json.dumps({"metric": "prefix cache: compression time with m of n row-blocks cached",
+    _emit({"metric": "prefix cache: compression time with m of n row-blocks cached",
                       "config": {"workload": "bf16 causal 8192 tokens, 16 layers, sender 32 heads, d=128, B=64",
                                  "tau": tau, "rowblocks": nb, "kept_blocks": full.nnz},
-                      "whole_sequence_ms": round(t_full, 3), "insert_ms": round(t_ins, 3), "rows": rows}))
+                      "whole_sequence_ms": round(t_full, 3), "insert_ms": round(t_ins, 3), "rows": rows})
 
 
 def fetch_overlap_bench(reps: int, tau: float):
@@ -216,12 +223,12 @@ def fetch_overlap_bench(reps: int, tau: float):
     out["bit_exact"] = bool(torch.equal(rp, full.row_ptr) and torch.equal(ci, full.col_idx)
                             and torch.equal(vals, full.values) and torch.equal(rst.block_mass, ref_mass))
     cache.release(keys, nb)
-    print(json.dumps({"metric": "cached-map fetch overlapped with the receiver's early-layer recompute",
+    _emit({"metric": "cached-map fetch overlapped with the receiver's early-layer recompute",
                       "config": {"workload": "bf16 causal 8192 tokens; fetch: 16 mapped layers x 32 sender heads, "
                                              "B=64, all 128 row-blocks cached; recompute stand-in: block statistics "
                                              "over 8 layers x 24 receiver heads, d=128",
                                  "tau": tau, "kept_blocks": full.nnz},
-                      "results": out}))
+                      "results": out})
 
 
 def headmix_fit_bench(reps: int, tau: float):
@@ -285,7 +292,7 @@ def headmix_fit_bench(reps: int, tau: float):
     executed = 2.0 * union * rows * cols * B * B
     useful = 2.0 * B * B * float(np.sum(s_cnt.astype(np.float64) ** 2 + r_cnt * s_cnt))
     fp64_peak = 78.6
-    print(json.dumps({"metric": "least-squares head-mix fit from compressed maps",
+    _emit({"metric": "least-squares head-mix fit from compressed maps",
                       "config": {"workload": "bf16 causal 8192 tokens, 16 layers; sender 32 heads, receiver 24 heads "
                                              "(own synthetic Q/K), B=64, both compressed at tau",
                                  "tau": tau, "sender_kept_blocks": sender.nnz, "receiver_kept_blocks": receiver.nnz,
@@ -294,7 +301,7 @@ def headmix_fit_bench(reps: int, tau: float):
                       "gram_executed_tflops": round(executed / t_gram / 1e9, 2),
                       "gram_useful_tflops": round(useful / t_gram / 1e9, 2),
                       "fp64_peak_tflops": fp64_peak,
-                      "gram_executed_frac": round(executed / t_gram / 1e9 / fp64_peak, 4)}))
+                      "gram_executed_frac": round(executed / t_gram / 1e9 / fp64_peak, 4)})
 
 
 def varlen_bench(reps: int):
@@ -343,12 +350,12 @@ def varlen_bench(reps: int):
             one(b)
 
     ms = _event_ms(all_steps, reps)
-    print(json.dumps({"metric": "whole path over every prefill chunk step, varlen / chunked / paged",
+    _emit({"metric": "whole path over every prefill chunk step, varlen / chunked / paged",
                       "config": {"workload": "bf16, 32 sequences lognormal(7.5, 0.8) lengths in [256, 16384], "
                                              "chunks of 2048 query rows, 16-token pages, 32 -> 24 heads, d=128, B=64",
                                  "layers_timed": L, "tau": wl.tau, "chunk_steps": len(steps),
                                  "query_rows": tot_q, "kept_blocks": int(sum(b[4] for b in steps))},
-                      "ms_all_steps": round(ms, 3), "tokens_per_s": round(tot_q / (ms * 1e-3), 1)}))
+                      "ms_all_steps": round(ms, 3), "tokens_per_s": round(tot_q / (ms * 1e-3), 1)})
 
 
 def several_receivers_bench(reps: int):
@@ -393,11 +400,11 @@ def several_receivers_bench(reps: int):
         o = f()
         torch.cuda.synchronize()
         res[name] = {"ms": round(_event_ms(f, reps), 3), "same_as_one_stream": all(torch.equal(a, b) for a, b in zip(o, ref))}
-    print(json.dumps({"metric": "fused mapped attention.V for two receivers of one compressed map",
+    _emit({"metric": "fused mapped attention.V for two receivers of one compressed map",
                       "config": {"workload": "bf16 causal 32768 tokens, sender 40 heads, d=128, B=128, receivers 32 and 24 heads",
                                  "tau": wl.tau, "kept_blocks": st.nnz,
                                  "kept_value_bytes": st.nnz * wl.B * wl.B * 2},
-                      "results": res}))
+                      "results": res})
 
 
 def pipelined_bench(reps: int, tau: float, layers: int, groups: int):
@@ -436,11 +443,11 @@ def pipelined_bench(reps: int, tau: float, layers: int, groups: int):
                          "same_as_one_group": bool(torch.equal(out, ref))}
         del pipe
         torch.cuda.synchronize()
-    print(json.dumps({"metric": "whole-path step over layer groups, fused step overlapped with the next group's statistics",
+    _emit({"metric": "whole-path step over layer groups, fused step overlapped with the next group's statistics",
                       "config": {"workload": f"bf16 causal 8192 tokens, {layers} mapped layers, sender 32 heads -> "
                                              "receiver 24 heads, d=128, B=64, structured Q/K",
                                  "tau": tau, "groups": groups, "timed_steps": reps},
-                      "results": res}))
+                      "results": res})
 
 
 def source_hash(rel: str) -> str:
@@ -700,7 +707,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, tau, min(args.cpu_sample_layers, L))
-    print(json.dumps(res), flush=True)
+    _emit(res)
 
 
 if __name__ == "__main__":
