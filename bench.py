@@ -523,7 +523,7 @@ def cpu_baseline(wl, tau, n_layers):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
 
