@@ -186,8 +186,9 @@ def test_repeat_calls_are_deterministic():
                                             (64, 64, 12, 9, None), (64, 64, 24, 8, None), (64, 64, 32, 8, None),
                                             (64, 64, 40, 8, None), (128, 64, 16, 8, None), (64, 128, 12, 8, None),
                                             (64, 128, 8, 8, None), (128, 128, 20, 24, None),
-                                            # half-stage ring: a head pair with one head past H_s
-                                            (64, 128, 31, 8, None),
+                                            # half-stage ring: a head pair with one head past H_s;
+                                            # 128-row blocks at d = 128
+                                            (64, 128, 31, 8, None), (128, 128, 32, 16, None),
                                             # grouped-query receivers: V staged per value head
                                             (64, 128, 32, 24, 8), (128, 128, 40, 32, 8), (64, 64, 24, 12, 4),
                                             (64, 128, 16, 16, 2), (128, 64, 8, 20, 5), (64, 128, 48, 16, 4)])
