@@ -193,6 +193,10 @@ class LayerGroupPipeline:
                                st.col_idx, st.values, cap, st.workspace, sync_count=False, stream=cur)
             if pipelined:
                 self.map_stream.wait_stream(cur)
+                # the caching allocator must not hand these out again while the
+                # second stream may still read or write them
+                for t in (st.row_ptr, st.col_idx, st.values, Wg, vg, og):
+                    t.record_stream(self.map_stream)
                 mf.mapped_attn_v(desc, self.batch, st.row_ptr, st.col_idx, st.values, Wg, vg, og,
                                  stream=self.map_stream)
             else:
