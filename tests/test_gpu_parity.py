@@ -121,7 +121,7 @@ def test_several_receivers_in_one_launch():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (32, 64)])
+@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (32, 64), (128, 128)])
 def test_several_receivers_varlen_paged_gqa(B, d):
     # grouped-query first receiver (6 heads over 3 value heads) and a 9-head
     # second one, paged values, varlen chunked batch, two layers
