@@ -2,6 +2,8 @@
 // gfx950 kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <atomic>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -11,6 +13,14 @@
 #include "mapflow.h"
 
 using mf::fail;
+
+namespace mf {
+
+static std::atomic<uint32_t> g_forced_portable{0};
+
+uint32_t forced_portable() { return g_forced_portable.load(std::memory_order_relaxed); }
+
+}  // namespace mf
 
 namespace {
 
@@ -123,7 +133,13 @@ const char* mf_status_string(mf_status s) {
 
 const char* mf_last_error_message(void) { return mf::error_buffer(); }
 
-const char* mf_version(void) { return "mapflow-mi355x 0.1"; }
+const char* mf_version(void) { return "mapflow-mi355x 0.2"; }
+
+uint32_t mf_debug_force_portable(uint32_t mask) {
+  const uint32_t all = MF_FORCE_PORTABLE_STATS | MF_FORCE_PORTABLE_SELECT | MF_FORCE_PORTABLE_EXTRACT |
+                       MF_FORCE_PORTABLE_MAPPED;
+  return mf::g_forced_portable.exchange(mask & all);
+}
 
 size_t mf_block_stats_workspace_size(const mf_sender_desc* desc, const mf_batch* batch) {
   if (!desc || !batch) return 0;
@@ -304,10 +320,7 @@ mf::MappedArgs mapped_args(const mf_receiver_desc* desc, const mf_batch* batch, 
   return a;
 }
 
-bool allow_fast_mapped() {
-  const char* pv = getenv("MF_PORTABLE_MAPPED");
-  return !(pv && pv[0] == '1');
-}
+bool allow_fast_mapped() { return !(mf::forced_portable() & MF_FORCE_PORTABLE_MAPPED); }
 
 }  // namespace
 

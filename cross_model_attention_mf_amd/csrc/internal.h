@@ -125,6 +125,9 @@ struct HeadmixArgs {
   int32_t layer_map[MF_MAX_LAYERS];
 };
 
+// Mask of stages forced onto their portable twins (mf_debug_force_portable).
+uint32_t forced_portable();
+
 // Launchers: return 0 on success, a hipError_t value otherwise.
 int launch_block_stats(const StatsArgs& a, mf_dtype dt, void* stream);
 size_t block_stats_lds_bytes(int B, int max_cb);

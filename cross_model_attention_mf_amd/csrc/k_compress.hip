@@ -12,8 +12,6 @@
 //            blocks only (MFMA), P = exp(S * scale - row_lse), and writes
 //            each B x B block key-major (values[e][key][query]) through LDS
 //            so every store is a full 16-byte vector.
-#include <stdlib.h>
-
 #include "device_common.h"
 #include "internal.h"
 
@@ -608,8 +606,7 @@ size_t select_lds_bytes(int max_cb) {
 int launch_select(const SelectArgs& a, void* stream) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
   const int n2 = next_pow2(a.b.max_cb < 1 ? 1 : a.b.max_cb);
-  const char* env = getenv("MF_PORTABLE_SELECT");
-  if (n2 <= 256 && !(env && env[0] == '1')) {
+  if (n2 <= 256 && !(forced_portable() & MF_FORCE_PORTABLE_SELECT)) {
     const long long nrows = (long long)a.L * a.H * a.b.total_rb;
     const dim3 grid((unsigned)((nrows + kSelWaves - 1) / kSelWaves));
     auto kern = n2 <= 64 ? select_wave_kernel<1> : n2 <= 128 ? select_wave_kernel<2> : select_wave_kernel<4>;
@@ -631,8 +628,7 @@ int launch_scan(const ScanArgs& a, void* stream) {
 
 bool extract_fast_path(mf_dtype dt, int B, int d) {
   if (dt != MF_BF16 || B != 64 || (d != 64 && d != 128)) return false;
-  const char* env = getenv("MF_PORTABLE_EXTRACT");
-  return !(env && env[0] == '1');
+  return !(forced_portable() & MF_FORCE_PORTABLE_EXTRACT);
 }
 
 size_t extract_mfma_lds_bytes(int d) { return (size_t)XNST * 64 * d * 2; }

@@ -16,8 +16,6 @@
 // and per column block, in fp64, mass_j = sum_r exp2(E[r][j] - lse2_r) / R.
 // Keeping E relative to the diagonal block's maximum keeps the important
 // blocks' log-masses small in magnitude, so fp32 holds them to ~1e-7.
-#include <stdlib.h>
-
 #include "device_common.h"
 #include "internal.h"
 
@@ -528,8 +526,7 @@ size_t block_stats_lds_bytes(int B, int max_cb) {
 
 bool stats_fast_path(mf_dtype dt, int B, int d) {
   if (dt != MF_BF16 || B != 64 || (d != 64 && d != 128)) return false;
-  const char* env = getenv("MF_PORTABLE_STATS");
-  return !(env && env[0] == '1');
+  return !(forced_portable() & MF_FORCE_PORTABLE_STATS);
 }
 
 static size_t stats_mfma_lds_bytes(int d) {

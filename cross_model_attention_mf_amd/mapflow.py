@@ -26,7 +26,10 @@ EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_mapped_attn_v", "mf_mapped_attn_v_multi", "mf_prefix_block_hashes", "mf_map_cache_create",
            "mf_map_cache_destroy", "mf_map_cache_insert", "mf_map_cache_lookup", "mf_map_cache_release",
            "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_headmix_workspace_size", "mf_headmix_gram",
-           "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version")
+           "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version",
+           "mf_debug_force_portable")
+# stages mf_debug_force_portable can send to their portable twins
+FORCE_PORTABLE = {"stats": 0x1, "select": 0x2, "extract": 0x4, "mapped": 0x8}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -145,8 +148,28 @@ def lib():
     L.mf_status_string.restype = ctypes.c_char_p
     L.mf_last_error_message.restype = ctypes.c_char_p
     L.mf_version.restype = ctypes.c_char_p
+    L.mf_debug_force_portable.argtypes = [ctypes.c_uint32]
+    L.mf_debug_force_portable.restype = ctypes.c_uint32
     _lib = L
     return L
+
+
+class force_portable:
+    """Context manager (tests only): calls inside it run the named stages
+    ("stats", "select", "extract", "mapped") on their portable twin kernels."""
+
+    def __init__(self, *stages: str):
+        self.mask = 0
+        for s in stages:
+            self.mask |= FORCE_PORTABLE[s]
+
+    def __enter__(self):
+        self.prev = int(lib().mf_debug_force_portable(self.mask))
+        return self
+
+    def __exit__(self, *exc):
+        lib().mf_debug_force_portable(self.prev)
+        return False
 
 
 def _check(status: int):

@@ -425,8 +425,20 @@ mf_status mf_map_cache_get_stats(const mf_map_cache* cache, mf_map_cache_stats* 
 const char* mf_status_string(mf_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char* mf_last_error_message(void);
-/* Library version, e.g. "mapflow-mi355x 0.1". */
+/* Library version, e.g. "mapflow-mi355x 0.2". */
 const char* mf_version(void);
+
+/* Cross-check hook for tests.  Every fast kernel has a portable twin that
+ * computes the same results with plain code (no MFMA, no async copies).  A
+ * set bit makes later calls, on every thread, take the twin of that stage;
+ * the calls' results are otherwise unchanged.  Returns the previous mask.
+ * The mask is process-wide and 0 by default: production callers never set
+ * it, and a change does not affect launches already queued. */
+#define MF_FORCE_PORTABLE_STATS   0x1u  /* mf_block_stats */
+#define MF_FORCE_PORTABLE_SELECT  0x2u  /* selection sort of mf_compress_blocks */
+#define MF_FORCE_PORTABLE_EXTRACT 0x4u  /* extraction of mf_compress_blocks */
+#define MF_FORCE_PORTABLE_MAPPED  0x8u  /* mf_mapped_attn_v, mf_mapped_attn_v_multi */
+uint32_t mf_debug_force_portable(uint32_t mask);
 
 #ifdef __cplusplus
 }

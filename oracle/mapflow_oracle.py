@@ -91,11 +91,6 @@ def num_candidates(rb: RowBlock, B: int) -> int:
     return rb.last_pos // B + 1
 
 
-def max_colblocks(cu_k: Sequence[int], B: int) -> int:
-    klens = np.diff(np.asarray(cu_k, dtype=np.int64))
-    return int(max(((int(n) + B - 1) // B for n in klens), default=0))
-
-
 # ----------------------------------------------------------------------------
 # 1. the sender's causal attention map (one head, one strip of query rows)
 # ----------------------------------------------------------------------------
@@ -272,7 +267,6 @@ def compress_unit(q: np.ndarray, k: np.ndarray, rb: RowBlock, h: int, B: int,
 @dataclasses.dataclass
 class LayerCompression:
     rowblocks: List[RowBlock]
-    max_cb: int
     units: Dict[Tuple[int, int], UnitResult]   # (h, rb.index) -> result
 
     def kept(self, h: int, rb: int) -> np.ndarray:
@@ -294,7 +288,7 @@ def compress_layer(q: np.ndarray, k: np.ndarray, cu_q, cu_k, q_pos0, B: int,
     for i in which:
         for h in hs:
             units[(h, i)] = compress_unit(q, k, rbs[i], h, B, tau, scale, keep_strips)
-    return LayerCompression(rbs, max_colblocks(cu_k, B), units)
+    return LayerCompression(rbs, units)
 
 
 def csr_of(lc: LayerCompression, H_s: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:

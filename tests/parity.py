@@ -216,3 +216,55 @@ def check_layer(run: GpuRun, li: int, rowblocks: Optional[Sequence[int]] = None,
         f"(|O|inf {rep.o_inf:.2e}) borderline={rep.borderline} kept={rep.kept_gpu}/{rep.kept_oracle} "
         f"oracle {time.time() - t0:.1f}s")
     return rep
+
+
+def check_csr(q_layers: Sequence[torch.Tensor], k_layers: Sequence[torch.Tensor], cu_q, cu_k, q_pos0,
+              B: int, tau: float, row_ptr: torch.Tensor, col_idx: torch.Tensor, values: torch.Tensor) -> int:
+    """Compare a compressed CSR (every layer, head and row-block, as
+    mf_compress_blocks numbers its rows) with the oracle run on the host
+    inputs q_layers[l] [Tq, H, d], k_layers[l] [Tk, H_kv, d].  Index sets must
+    pass accept_set; values the per-dtype tolerance of check_layer.  Returns
+    the number of borderline blocks."""
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy()
+    is_bf16 = values.dtype == torch.bfloat16
+    H = q_layers[0].shape[1]
+    border = 0
+    for li, (ql, kl) in enumerate(zip(q_layers, k_layers)):
+        q64, k64 = synth.to_f64(ql), synth.to_f64(kl)
+        lc = orc.compress_layer(q64, k64, cu_q, cu_k, q_pos0, B, tau)
+        nrb = len(lc.rowblocks)
+        for h in range(H):
+            for i in range(nrb):
+                row = (li * H + h) * nrb + i
+                e0, e1 = int(rp[row]), int(rp[row + 1])
+                cols = ci[e0:e1]
+                u = lc.units[(h, i)]
+                ok, ndiff, bad = orc.accept_set(u.sel, cols, SET_EPS)
+                assert ok, f"layer {li} head {h} rowblock {i}: gpu {cols.tolist()} oracle {u.sel.kept.tolist()}"
+                border += ndiff
+                if ndiff:
+                    u = orc.compress_unit(q64, k64, lc.rowblocks[i], h, B, tau, orc.default_scale(q64.shape[2]),
+                                          keep_strip=True)
+                got = values[e0:e1].to(torch.float64).cpu().numpy().transpose(0, 2, 1)
+                for t, j in enumerate(cols):
+                    want = u.block(int(j), B) if ndiff else u.values[list(u.sel.kept).index(j)]
+                    tol = (2.0 ** -8 * np.abs(want) + 1e-30) if is_bf16 else (VAL_RTOL_F32 * np.abs(want) + 1e-9)
+                    assert np.all(np.abs(got[t] - want) <= tol), f"values of layer {li} head {h} rowblock {i} block {j}"
+    assert int(rp[0]) == 0 and int(rp[-1]) == ci.shape[0], "row_ptr must run from 0 to the entry count"
+    return border
+
+
+def check_masses(q: torch.Tensor, k: torch.Tensor, cu_q, cu_k, B: int, block_mass: torch.Tensor,
+                 rowblocks: Sequence[int]) -> float:
+    """Block masses of one layer (q [Tq, H, d], k host tensors) on the given
+    row-blocks against the oracle; returns the largest error."""
+    q64, k64 = synth.to_f64(q), synth.to_f64(k)
+    lc = orc.compress_layer(q64, k64, cu_q, cu_k, None, B, 1.0, rowblocks=rowblocks)
+    got = block_mass.cpu().numpy()
+    err = 0.0
+    for (h, i), u in lc.units.items():
+        n = len(u.sel.masses)
+        err = max(err, float(np.max(np.abs(got[h, i, :n] - u.sel.masses))))
+    assert err <= MASS_TOL, f"block mass error {err:.3e}"
+    return err

@@ -331,3 +331,13 @@ def test_layer_group_pipeline_rejects_bad_group_counts():
     for g in (0, 5):
         with pytest.raises(ValueError):
             pipeline.LayerGroupPipeline(None, q, q, q, None, None, 64, 0.9, 2, g)
+
+
+def test_force_portable_hook_round_trip():
+    L = mf.lib()
+    assert L.mf_debug_force_portable(0) == 0
+    with mf.force_portable("stats", "mapped"):
+        # unknown bits are dropped; the previous mask comes back
+        assert L.mf_debug_force_portable(0xFFFFFFFF) == 0x9
+        assert L.mf_debug_force_portable(0x9) == 0xF
+    assert L.mf_debug_force_portable(0) == 0

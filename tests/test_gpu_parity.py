@@ -192,13 +192,13 @@ def test_repeat_calls_are_deterministic():
                                             # grouped-query receivers: V staged per value head
                                             (64, 128, 32, 24, 8), (128, 128, 40, 32, 8), (64, 64, 24, 12, 4),
                                             (64, 128, 16, 16, 2), (128, 64, 8, 20, 5), (64, 128, 48, 16, 4)])
-def test_portable_and_mfma_mapped_kernels_agree_with_oracle(monkeypatch, B, d, Hs, Hr, Hkv):
+def test_portable_and_mfma_mapped_kernels_agree_with_oracle(B, d, Hs, Hr, Hkv):
     wl = tiny_structured("bf16", workload_id=14, B=B, d=d, H_s=Hs, H_r=Hr, H_kv_r=Hkv,
                          seqlens=(4 * B + 9, B + 3), num_layers=1)
     runs = []
-    for portable in ("1", "0"):
-        monkeypatch.setenv("MF_PORTABLE_MAPPED", portable)
-        run = parity.run_gpu(wl, 0.9, [0])
+    for stages in (("mapped",), ()):
+        with mf.force_portable(*stages):
+            run = parity.run_gpu(wl, 0.9, [0])
         parity.check_layer(run, 0)
         runs.append(run.outs[0].float())
     # both kernels compute the same sums in a different order
@@ -206,16 +206,16 @@ def test_portable_and_mfma_mapped_kernels_agree_with_oracle(monkeypatch, B, d, H
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_portable_and_mfma_block_stats_agree_with_oracle(monkeypatch, d):
+def test_portable_and_mfma_block_stats_agree_with_oracle(d):
     # varlen chunked batch: groups of four row-blocks cut short by sequence
     # ends, a one-row tail block, a sequence shorter than one block, several
     # (layer, head) pairs per XCD queue, and chunk rows starting past 0
     wl = tiny_structured("bf16", workload_id=15, B=64, d=d, H_s=12, H_r=4, num_layers=2,
                          seqlens=(64 * 9 + 17, 64 * 2 + 1, 63, 64 * 5, 700), chunk=256)
     results = []
-    for portable in ("1", "0"):
-        monkeypatch.setenv("MF_PORTABLE_STATS", portable)
-        run = parity.run_gpu(wl, 0.9, [0, 1], step=1)
+    for stages in (("stats",), ()):
+        with mf.force_portable(*stages):
+            run = parity.run_gpu(wl, 0.9, [0, 1], step=1)
         for li in range(2):
             parity.check_layer(run, li)
         results.append((run.state.row_lse.clone(), run.state.block_mass.clone()))
@@ -227,15 +227,15 @@ def test_portable_and_mfma_block_stats_agree_with_oracle(monkeypatch, d):
 @pytest.mark.parametrize("B,seqlens", [(64, (64 * 9 + 17, 63, 700)),          # up to 64 candidates per row
                                        (32, (32 * 120 + 5, 40)),              # up to 128
                                        (32, (32 * 250 + 31, 32 * 3))])         # up to 256
-def test_wave_and_workgroup_selection_agree(monkeypatch, B, seqlens):
+def test_wave_and_workgroup_selection_agree(B, seqlens):
     """The one-wave-per-row selection and the workgroup sort give the same
     CSR; the run is also checked against the oracle."""
     wl = tiny_structured("bf16", workload_id=16, B=B, d=64, H_s=6, H_r=4, seqlens=seqlens)
     runs = []
-    for portable in ("1", "0"):
-        monkeypatch.setenv("MF_PORTABLE_SELECT", portable)
-        for tau in (0.5, 0.95):
-            runs.append(parity.run_gpu(wl, tau, [0]))
+    for stages in (("select",), ()):
+        with mf.force_portable(*stages):
+            for tau in (0.5, 0.95):
+                runs.append(parity.run_gpu(wl, tau, [0]))
     nrb = runs[-1].state.batch.total_rowblocks
     parity.check_layer(runs[-1], 0, rowblocks=parity.sample_rowblocks(nrb, 12))
     for a, b in zip(runs[:2], runs[2:]):
@@ -246,16 +246,16 @@ def test_wave_and_workgroup_selection_agree(monkeypatch, B, seqlens):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_portable_and_mfma_extraction_agree_with_oracle(monkeypatch, d):
+def test_portable_and_mfma_extraction_agree_with_oracle(d):
     """bf16, B = 64: the MFMA extraction and its portable twin write the same
     CSR; their values (each rounded to bf16 from its own fp32 scores) agree to
     a bf16 rounding step, and both match the oracle."""
     wl = tiny_structured("bf16", workload_id=17, B=64, d=d, H_s=6, H_r=4,
                          seqlens=(64 * 5 + 9, 64 * 2, 33), chunk=None)
     runs = []
-    for portable in ("1", "0"):
-        monkeypatch.setenv("MF_PORTABLE_EXTRACT", portable)
-        run = parity.run_gpu(wl, 0.9, [0])
+    for stages in (("extract",), ()):
+        with mf.force_portable(*stages):
+            run = parity.run_gpu(wl, 0.9, [0])
         parity.check_layer(run, 0)
         runs.append(run.state)
     a, b = runs

@@ -217,11 +217,14 @@ def test_eviction_is_lru_and_skips_pinned_entries():
 
 def test_fetch_overlapped_with_other_work_is_exact():
     """Splices run stream-ordered on a side stream while other kernels run on
-    the current stream; back-to-back calls reuse the staging area."""
+    the current stream; back-to-back calls reuse the staging area.  The
+    spliced CSR is checked against the oracle, and so are the masses of the
+    work that ran beside the fetch."""
     B, d, tau = 64, 128, 0.9
     T = 7 * B + 19
     wl = seq_workload("bf16", B, d, T, wid=29)
     q, k = seq_qk(wl)
+    q_host, k_host = q.cpu(), k.cpu()
     full = compress_rows(q, k, B, tau)
     keys = mf.prefix_block_hashes(tokens_of(T, 11), B)
     cache = mf.MapCache(q.dtype, 2, wl.H_s, B, 64 << 20)
@@ -237,6 +240,9 @@ def test_fetch_overlapped_with_other_work_is_exact():
     other()
     torch.cuda.synchronize()
     ref_mass = ost.block_mass.clone()
+    nrb_o = ob.total_rowblocks
+    parity.check_masses(oq[0].cpu(), ok[0].cpu(), [0, 4 * T], [0, 4 * T], B, ref_mass[0],
+                        [0, nrb_o // 2, nrb_o - 1])
     side = torch.cuda.Stream()
     for m in (4, 7, 7):
         assert cache.lookup(keys[:m]) == m
@@ -250,4 +256,6 @@ def test_fetch_overlapped_with_other_work_is_exact():
         cache.release(keys[:m], m)
         assert_same_csr((nnz, rp, ci, vals), full)
         assert torch.equal(ost.block_mass, ref_mass)
+        if m == 4:
+            parity.check_csr(list(q_host), list(k_host), [0, T], [0, T], None, B, tau, rp, ci[:nnz], vals[:nnz])
     cache.close()

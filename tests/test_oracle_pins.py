@@ -450,3 +450,60 @@ def test_prefix_block_keys_depend_on_the_prefix_only():
     assert keys[0] == ph.fnv1a_64(data)
     # a trailing partial block gets no key
     assert len(ph.prefix_block_keys(toks[:16 * 3 + 5], 16)) == 3
+
+
+# ------------------------------------------------ pins: CSR order of a layer
+
+def _hand_layer():
+    """Two sender heads x three row-blocks of 32 rows with kept sets chosen by
+    hand; every value of block t of (head h, row-block i) is 100 h + 10 i + t,
+    so the position of each block in the CSR shows which unit it came from."""
+    B = 32
+    kept = {(0, 0): [0], (0, 1): [0, 1], (0, 2): [0, 2],
+            (1, 0): [0], (1, 1): [1], (1, 2): [0, 1, 2]}
+    rbs = orc.enumerate_rowblocks([0, 96], [0, 96], None, B)
+    units = {}
+    for (h, i), ks in kept.items():
+        n = i + 1
+        rest = [j for j in range(n) if j not in ks]
+        sel = orc.Selection(np.zeros(n), np.asarray(ks + rest), np.zeros(n + 1), len(ks), 0.5)
+        vals = np.stack([np.full((B, B), 100.0 * h + 10 * i + t) for t in range(len(ks))])
+        units[(h, i)] = orc.UnitResult(np.zeros(B), sel, vals)
+    return orc.LayerCompression(rbs, units)
+
+
+# The library numbers CSR row (layer l, head h, row-block i) as
+# (l * H_s + h) * total_rowblocks + i: head-major, row-blocks fastest.  For the
+# hand layer above that order is (0,0) (0,1) (0,2) (1,0) (1,1) (1,2).
+HAND_ROW_PTR = [0, 1, 3, 5, 6, 7, 10]
+HAND_COL_IDX = [0, 0, 1, 0, 2, 0, 1, 0, 1, 2]
+HAND_MARKERS = [0, 10, 11, 20, 21, 100, 110, 120, 121, 122]
+
+
+def check_csr_order():
+    row_ptr, col_idx, values = orc.csr_of(_hand_layer(), 2)
+    return (row_ptr.tolist() == HAND_ROW_PTR and col_idx.tolist() == HAND_COL_IDX
+            and values[:, 0, 0].tolist() == HAND_MARKERS
+            and bool(np.all(values == values[:, :1, :1])))
+
+
+def test_csr_of_is_head_major_with_ascending_columns():
+    assert check_csr_order()
+
+
+def test_planted_rowblock_major_csr(monkeypatch):
+    def bad(lc, H_s):
+        nrb = len(lc.rowblocks)
+        row_ptr = np.zeros(H_s * nrb + 1, dtype=np.int64)
+        cols, vals = [], []
+        r = 0
+        for i in range(nrb):
+            for h in range(H_s):
+                u = lc.units[(h, i)]
+                row_ptr[r + 1] = row_ptr[r] + u.sel.kstar
+                r += 1
+                cols.append(u.sel.kept)
+                vals.append(u.values)
+        return row_ptr, np.concatenate(cols), np.concatenate(vals)
+    _with(monkeypatch, "csr_of", bad)
+    assert not check_csr_order()
