@@ -7,6 +7,8 @@
 // row-block, receiver head).  Wave 0 merges the sender heads' sorted column
 // lists into their union, one block at a time; the mixed block
 // A = sum_h W[r][h] P_h is formed in LDS (fp32) and multiplied by the V tile.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -102,54 +104,52 @@ __global__ void __launch_bounds__(kMapThreads) mapped_generic_kernel(MappedArgs 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16).  One workgroup per (receiver layer, row-block, 64-row
-// half of a 128-row block, group of 8 receiver heads); 2 x RQ/16 waves, wave
-// (hq, qt) owning receiver heads 4hq..4hq+3 of the group and query rows
-// 16qt..16qt+15.  Each block j of the union of the sender heads' kept sets is
-// walked in 32-key steps; a step is 4 stages g2 = 0..3, and stage g2 stages
-// the 8 keys 32cb + 8 g2 + e (e = 0..7) of every sender head in LDS.
+// MFMA kernel (bf16, B = 64 or 128).  One workgroup of 8 waves per (receiver
+// layer, row-block, 64-row half of a 128-row block, group of 8 receiver
+// heads).  The union of the sender heads' kept blocks is walked in 4-key
+// stages; for every stage:
 //
-//   head mix (MFMA 16x16x32, K = sender heads, W block-diagonal in the key
-//   group):  C_e[(g, r)][q] += sum_h [g == g2] W[r][h] P_h[32cb + 8 g2 + e][q]
-//   so lane (g, q) holds, for e = 0..7, the mixed map A_r[q][32cb + 8g + e]:
-//   exactly the A operand (8 keys per lane group) of the P.V MFMA, and the
-//   mixed map never leaves registers.
-//   P.V (MFMA 16x16x32, K = keys): O_r[q][n] += A_r[q][c] V_r[c][n].
+//   head mix (MFMA 16x16x32, K = sender heads, 32 per chunk):
+//     A^T[(c, q)][r] = sum_h P_h[c][q] W[r][h]
+//     wave w mixes key 4 s + w / 2 for queries 32 (w & 1) .. + 31; the 16
+//     positions of one MFMA are 16 consecutive queries of one key (the
+//     transposing LDS read hands lane t the sender heads of query t), the
+//     16 columns are the group's receiver heads (8, padded to 16).  Each lane
+//     then holds four consecutive queries of one receiver head and stores
+//     them as one 8-byte write into the mixed-map buffer A[r][key][q].
+//   P.V (MFMA 32x32x16, K = 16 keys): wave w owns receiver head 8 g + w for
+//     all 64 rows and d, O_r[q][n] += A_r[q][c] V_r[c][n], once every four
+//     stages, over the 16 keys the four stages mixed.
 //
-// Two memory pipelines; key-major block rows (RQ contiguous queries) are
-// copied HBM -> LDS with global_load_lds (16 bytes per lane, no registers).
+// So every staged value of P, of the mixed map and of V is read from LDS
+// exactly once per workgroup, and the mixed map never leaves the chip.
 //
-// Half-stage ring (when the sender heads, padded to a multiple of 16, leave
-// room for five 4-key slots beside a 32-key V buffer): stage s mixes the
-// half-stages 2s and 2s+1 and, right after the barrier that opens it, issues
-// 2s+3 and 2s+4 into the slots stage s-1 consumed, so one and a half stages
-// are in flight.  A slot holds 4 key rows per head, unpadded; odd heads hold
-// each key pair swapped, so a transpose read of one key meets neighbouring
-// heads in opposite bank halves.  One copy covers a pair of heads.  The V
-// rows of a 32-key step arrive at its first stage, and P.V runs once per
-// step, after stage 3, over all 32 keys.
+// Memory pipeline: kept values (key-major rows of 64 queries, 128 bytes) and
+// V rows move HBM -> LDS with global_load_lds (16 bytes per lane, no
+// registers).  P stages sit in an NS-slot ring; the copies of stage s + NS - 1
+// are issued right after the barrier that opens stage s, into the slot stage
+// s - 1 consumed.  V rows of a 16-key step arrive in one of NVB buffers: with
+// two, step t's rows are issued at its first stage and P.V of step t runs
+// spread over the four stages of step t + 1 (one 32-wide n tile per stage);
+// with one, they are issued at the second stage of step t and P.V of step t
+// runs whole at the first stage of step t + 1.  One counted vmcnt wait plus
+// one barrier per stage: every wave issues its P copies last, so the wait
+// covers the rows of the stage about to be mixed and every older copy.
+// Sender heads that do not keep a block issue no copy: their rows in the
+// ring keep finite values of an earlier block (or the initial zeros) and meet
+// a zero weight.  Keys past the sequence read a valid V row whose finite
+// values meet zero probabilities.  The union merge runs on wave 0, two
+// blocks ahead, with the next column of each sender head arriving through an
+// async copy.  The copies are inline assembly, which the compiler does not
+// track, so it inserts no drain of the ring before LDS accesses; the kernel's
+// own waits and barriers order them.
 //
-// Stage ring (other shapes): a 3-slot ring of 8-key stages (2 when the
-// sender heads leave LDS for only two), each head's rows padded by 128 bytes:
-// the copies of stage s + 2 are issued at stage s.  Key groups not yet mixed
-// are still zero, so P.V runs twice per step, after stages 1 and 3, each
-// time over the 16 keys whose V rows are in LDS.  The V rows of a 16-key
-// half arrive in their own buffer, issued at the half's first stage and used
-// after its second (or one half ahead with two buffers).  V rows are staged once per
-// value head the group's receiver heads read (grouped-query receivers share
-// them), not once per receiver head.  Only sender heads that keep the block
-// issue P copies; the slot of an absent head keeps finite values from an
-// earlier block (or the initial zeros), which meet a zero weight.  Every
-// stage issues its P copies last, so one counted wait at the top of each
-// stage (vmcnt = the wave's newest P copies, a wave-uniform count; 0 with a
-// 2-slot ring) covers the rows the stage reads and the V rows of its step.  The copies are issued as inline
-// assembly, which the compiler does not track, so it inserts no drain of the
-// ring before LDS accesses; the kernel's own waits and barriers order them.
-// The column lists of the sender heads and the page ids of paged values also
-// arrive through async LDS copies.  Keys past the sequence read a valid row
-// whose finite values meet zero probabilities.  Operands are read
-// with ds_read_tr16_b64 (lane t of a 16-lane group gets column t of a 4-row
-// tile) from rows whose 16-byte chunks are XOR-swizzled.
+// LDS swizzles (16-byte chunks, 64 banks of 4 bytes):
+//   P ring [head][4 keys][64 q]: head h keeps its key rows in pair order
+//     flipped by gp(h) and its chunks XOR fp(h), so the 16 heads one
+//     transposing read touches spread over both bank halves;
+//   A [r][16 keys][64 q], head stride 16 * 128 + 32 bytes: chunks XOR sa(key);
+//   V [value head][16 keys][d]: chunks XOR sv(key).
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -180,48 +180,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// wait until at most n (wave-uniform, 0 <= n <= M) vector memory operations
-// of this wave are outstanding
-template <int M>
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  static_assert(M <= 15, "wait range");
-  switch (n < M ? n : M) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<M>(); break;
-  }
+// chunk / row swizzles (see above)
+__host__ __device__ constexpr int fp_swz(int h) { return 2 * ((h & 1) | (((h >> 3) & 1) << 1)); }
+__host__ __device__ constexpr int gp_swz(int h) { return (h >> 1) & 1; }
+__host__ __device__ constexpr int sa_swz(int key) { return 4 * (((key >> 1) ^ (key >> 3)) & 1); }
+template <int D>
+__host__ __device__ constexpr int sv_swz(int key) {
+  return D == 128 ? 4 * ((key & 3) ^ ((key >> 2) & 3)) : 4 * (((key >> 1) ^ (key >> 3)) & 1);
 }
-
-// A copy of a lane value the compiler cannot see through: per-stage address
-// math derived from it is recomputed in place (a few VALU ops) instead of
-// being hoisted out of the stage loop and pinned in registers.
-__device__ __forceinline__ int opaque(int x) {
-  int y;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-  return y;
-}
-
-// P rows of one head (8 keys x RQ queries) sit in a group padded by 128
-// bytes, so heads of opposite parity start half an LDS bank cycle apart, and
-// each head's 16-byte chunks are XOR-swizzled by swz_p(h): the 16 heads one
-// transpose read touches (4 per 16-lane group, 32 bytes each) then cover all
-// 64 banks.  V rows (one key, D values) are swizzled by swz_v(row), which
-// gives the 8 rows read together 8 distinct chunk pairs.
-__host__ __device__ constexpr int swz_p(int h) { return 2 * (((h >> 1) & 1) | (((h >> 3) & 1) << 1)); }
-__device__ __forceinline__ int swz_v(int row, int cpr) { return (2 * ((row & 3) | (((row >> 3) & 1) << 2))) & (cpr - 1); }
 
 struct alignas(16) UnionInfo {
   int j;
@@ -231,47 +197,60 @@ struct alignas(16) UnionInfo {
   int page[128];
 };
 
-constexpr size_t kMapMeta = 2 * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
+constexpr int kUnionSlots = 3;
+constexpr size_t kMapMeta = kUnionSlots * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
+constexpr int kMapWaves = 8;
+constexpr int kMapRows = 64;   // query rows per workgroup
 
-template <int B, int D, int HP8, int KVC>
+// LDS plan of the MFMA kernel
+template <int B, int D, int HP, int KVC, int NS, int NVB>
 struct MapCfg {
-  static_assert(B >= 64, "the MFMA kernel covers 64-row query tiles");
-  static constexpr int RQ = 64;                        // query rows per workgroup
-  static constexpr int NQT = RQ / 16;                  // query tiles
-  static constexpr int NW = 2 * NQT;                   // waves
-  static constexpr int NT = D / 16;                    // 16-wide n tiles of d
-  static constexpr int CB = B / 32;                    // 32-key steps per block
-  static constexpr int SPU = 4 * CB;                   // 8-key stages per block
-  static constexpr int QH = B / RQ;                    // workgroups per row-block
-  static constexpr int PROW = RQ * 2;                  // bytes per P row (one key, RQ queries)
-  static constexpr int HSTR = 8 * PROW + 128;          // bytes per head group of 8 P rows
-  static constexpr int VROW = D * 2;                   // bytes per V row
-  static constexpr int VCPR = VROW / 16;
-  static constexpr int VB = KVC * 16 * VROW;           // one V buffer: KVC value heads x 16 keys
-  static constexpr int HPAD = 8 * HP8;
-  static constexpr int SBYTES = HPAD * HSTR;           // one stage: 8 keys x all heads
-  static constexpr bool fits(int ns, int nv) { return (size_t)ns * SBYTES + (size_t)nv * VB + kMapMeta <= 163840; }
-  static constexpr int NSLOT = fits(3, 2) || fits(3, 1) ? 3 : 2;  // P ring slots
-  static constexpr int NVB = fits(NSLOT, 2) ? 2 : 1;   // V buffers
-  static constexpr int VBYTES = NVB * VB;
-  static constexpr int AHEAD = NSLOT - 1;              // stages issued ahead of the mix
-  static constexpr int PW = HPAD / NW;                 // P copy instructions (heads) per wave per stage
-  static constexpr int RPI = 1024 / VROW;              // V rows per copy instruction
-  static_assert(HPAD % NW == 0, "P copies must split evenly over the waves");
-  static_assert(16 % RPI == 0, "a value head's 16 rows fill whole copy instructions");
-  // half-stage ring: NHS slots of 4 key rows per head, unpadded, beside a
-  // V buffer of 32 keys (P.V then covers 32 live keys)
-  static constexpr int NHS = 5;
-  static constexpr int HSB = HPAD * 4 * PROW;          // one half-slot
-  static constexpr int VB32 = KVC * 32 * VROW;
-  static constexpr bool HALF = (HPAD / 2) % NW == 0 && (size_t)NHS * HSB + (size_t)VB32 + kMapMeta <= 163840;
-  static constexpr int PWH = HPAD / 2 / NW;            // head-pair copies per wave per half-stage
-  static constexpr int HPU = B / 4;                    // half-stages per block
-  static constexpr int RING = HALF ? NHS * HSB : NSLOT * SBYTES;
-  static constexpr int VK = HALF ? 32 : 16;            // keys per V buffer
-  static constexpr int VBUF = HALF ? VB32 : VB;
-  static constexpr int VTOT = HALF ? VB32 : VBYTES;
+  static_assert(B == 64 || B == 128, "64- or 128-row blocks");
+  static_assert(HP % 16 == 0 && HP >= 16 && HP <= 64, "sender heads padded to 16");
+  static_assert(NS >= 2 && NS <= 5 && (NVB == 1 || NVB == 2), "ring plan");
+  static constexpr int QH = B / kMapRows;            // workgroups per row-block
+  static constexpr int SPB = B / 4;                  // 4-key stages per block
+  static constexpr int SB = B / 16;                  // 16-key steps per block
+  static constexpr int PROW = kMapRows * 2;          // bytes of one key row of P (64 queries)
+  static constexpr int SLOT = HP * 4 * PROW;         // one stage: HP heads x 4 keys
+  static constexpr int VROW = D * 2;
+  static constexpr int VCPR = VROW / 16;             // 16-byte chunks per V row
+  static constexpr int VRPI = 1024 / VROW;           // V rows per copy instruction
+  static constexpr int VB = KVC * 16 * VROW;         // V rows of one 16-key step
+  static constexpr int VC = KVC * 16 / VRPI / kMapWaves;   // V copy instructions per wave and step
+  static constexpr int AHS = 16 * PROW + 32;         // mixed map of one receiver head, padded
+  static constexpr int AB = 8 * AHS;
+  static constexpr int VOFF = NS * SLOT;
+  static constexpr int AOFF = VOFF + NVB * VB;
+  static constexpr int MAIN = AOFF + AB;
+  static constexpr int OST = kMapRows * 8 * D * 2;   // output staging (aliases the buffers above)
+  static constexpr int MAINX = ((MAIN > OST ? MAIN : OST) + 15) / 16 * 16;
+  static constexpr size_t LDS = (size_t)MAINX + kMapMeta;
+  static constexpr int PCW = HP / 16;                // P copy instructions (head pairs) per wave and stage
+  static constexpr int NKC = (HP + 31) / 32;         // 16x16x32 chunks of sender heads (the last may be half)
+  static constexpr int NT = D / 32;                  // 32-wide n tiles of d
+  static constexpr int VPART = NVB == 2 ? 0 : 1;     // stage of a step that issues the step's V rows
+  static_assert(16 % VRPI == 0 && VC * VRPI * kMapWaves == KVC * 16, "V rows fill whole copy instructions");
+  // copies one wave issues at stage p of a step (P copies and V rows), and
+  // how many may still be in flight when stage p opens: those of the NS - 2
+  // stages issued after the copies of stage p
+  static constexpr int ops(int p) { return PCW + (p == VPART ? VC : 0); }
+  static constexpr int allow(int p) {
+    int n = 0;
+    for (int b = 1; b <= NS - 2; ++b) n += ops((p - b + 8) & 3);
+    return n;
+  }
 };
+
+size_t map_lds_bytes(int B, int D, int HP, int KVC, int NS, int NVB) {
+  const size_t prow = 128, slot = (size_t)HP * 4 * prow, vb = (size_t)KVC * 16 * D * 2;
+  const size_t ab = 8 * (16 * prow + 32);
+  const size_t main = NS * slot + NVB * vb + ab;
+  const size_t ost = (size_t)kMapRows * 8 * D * 2;
+  const size_t mainx = ((main > ost ? main : ost) + 15) / 16 * 16;
+  (void)B;
+  return mainx + kMapMeta;
+}
 
 // value heads one group of 8 receiver heads reads, at most over the groups
 int group_value_heads(int Hr, int Hkv) {
@@ -285,46 +264,31 @@ int group_value_heads(int Hr, int Hkv) {
   return mx;
 }
 
-size_t mapped_mfma_lds_bytes(int B, int D, int Hs, int kvc) {
-  if (B < 64) return (size_t)1 << 40;                  // no MFMA kernel for 32-row blocks
-  const size_t hpad = (size_t)(Hs + 7) / 8 * 8;
-  const size_t stage = hpad * (8 * 128 + 128);
-  const size_t vb = (size_t)kvc * 16 * D * 2;
-  auto fits = [&](size_t ns, size_t nv) { return ns * stage + nv * vb + kMapMeta <= 163840; };
-  const size_t nslot = fits(3, 2) || fits(3, 1) ? 3 : 2;
-  const size_t nvb = fits(nslot, 2) ? 2 : 1;
-  const size_t obytes = (size_t)64 * 8 * D * 2;       // output staging (aliases the ring and V)
-  size_t main = nslot * stage + nvb * vb;
-  const size_t hsb = hpad * 4 * 128, vb32 = (size_t)kvc * 32 * D * 2;
-  if (hpad % 16 == 0 && 5 * hsb + vb32 + kMapMeta <= 163840) main = 5 * hsb + vb32;
-  if (obytes > main) main = obytes;
-  return main + kMapMeta;
-}
-
 // column of an exhausted sender head (the merge copies it instead of a
 // col_idx entry)
 __device__ const int kNoColumn = 0x7FFFFFFF;
 
-template <int B, int D, int HP8, int KVC>
-__global__ void __launch_bounds__(((B < 64 ? B : 64) / 16) * 2 * 64)
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <int B, int D, int HP, int KVC, int NS, int NVB>
+__global__ void __launch_bounds__(kMapWaves * 64)
 mapped_mfma_kernel(MappedArgs a, int ngroups) {
-  using C = MapCfg<B, D, HP8, KVC>;
-  constexpr int hpad = C::HPAD;
+  using C = MapCfg<B, D, HP, KVC, NS, NVB>;
   extern __shared__ __align__(16) char smem[];
-  char* ring = smem;
-  char* Vs = smem + C::RING;
-  size_t main_bytes = C::RING + C::VTOT;
-  if ((size_t)C::RQ * 8 * D * 2 > main_bytes) main_bytes = (size_t)C::RQ * 8 * D * 2;
-  UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + main_bytes);
-  int* curcol = reinterpret_cast<int*>(UI + 2);        // next column of each sender head
-  float* Wsh = reinterpret_cast<float*>(curcol + 64);   // [8 receiver heads][64 sender heads]
+  char* const ring = smem;
+  char* const vbuf = smem + C::VOFF;
+  char* const abuf = smem + C::AOFF;
+  UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + C::MAINX);
+  int* curcol = reinterpret_cast<int*>(UI + kUnionSlots);   // next column of each sender head
+  float* Wsh = reinterpret_cast<float*>(curcol + 64);        // [8 receiver heads][64 sender heads]
 
   // ---- work item.  A unit is one (row-block part, receiver layer); its head
   // groups (those of every receiver of the launch) run back to back on one
   // XCD (workgroup b runs on XCD b % 8), so they share that XCD's L2 for the
-  // kept values.  Units are dealt to the
-  // XCDs in turn, latest row-blocks first: a row-block's union (and work)
-  // grows with its causal range, and the short ones then fill the tail.
+  // kept values.  Units are dealt to the XCDs in turn, latest row-blocks
+  // first: a row-block's union (and work) grows with its causal range, and
+  // the short ones then fill the tail.
   const int nitems = a.b.total_rb * C::QH;
   int item, grp, l;
   {
@@ -341,18 +305,19 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   for (int k = 1; k < a.nrecv; ++k) rk = grp >= a.rx[k].group0 ? k : rk;
   const MappedRecv R = a.rx[rk];
   grp -= R.group0;
-  const int rb = item / C::QH, qoff = (item % C::QH) * C::RQ;
+  const int rb = item / C::QH, qoff = (item % C::QH) * kMapRows;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, B, rb);
   const int sl = a.layer_map[l];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hq = wave / C::NQT, qt = wave % C::NQT;
-  const int lg = lane >> 4, lr = lane & 15;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lg = lane >> 4, l16 = lane & 15, lh = lane >> 5;
   const bool paged = R.block_table != nullptr;
 
-  // ---- zero the ring and V rows, load the group's W rows
-  for (size_t o = (size_t)tid * 16; o < main_bytes; o += (size_t)C::NW * 64 * 16)
+  // ---- clear the ring and the V / mixed-map buffers (finite values for
+  // rows no copy writes), load the group's W rows
+  for (int o = tid * 16; o < C::MAIN; o += kMapWaves * 64 * 16)
     *reinterpret_cast<uint4*>(smem + o) = make_uint4(0, 0, 0, 0);
-  for (int t = tid; t < 8 * 64; t += C::NW * 64) {
+  for (int t = tid; t < 8 * 64; t += kMapWaves * 64) {
     const int rl = t >> 6, h = t & 63, r = 8 * grp + rl;
     Wsh[t] = (h < a.Hs && r < R.Hr) ? R.W[((size_t)l * R.Hr + r) * a.Hs + h] : 0.f;
   }
@@ -360,7 +325,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // ---- union merge state (wave 0): lane h walks sender head h's sorted list
   int64_t mptr = 0, mend = 0;
   if (wave == 0) {
-    int c0 = 0x7FFFFFFF;
+    int c0 = kNoColumn;
     if (lane < a.Hs) {
       const size_t row = ((size_t)sl * a.Hs + lane) * a.b.total_rb + rb;
       mptr = min((int64_t)a.row_ptr[row], a.csr_capacity);
@@ -372,12 +337,11 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // wave 0: next block of the union and the heads that keep it; the heads'
   // next columns and the block's page ids arrive asynchronously in LDS
   auto merge = [&](UnionInfo* out) {
-    int copies = 1;
     const int mcur = curcol[lane];
     int jm = mcur;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) jm = min(jm, __shfl_xor(jm, off, 64));
-    const bool take = (mcur == jm) && (mcur != 0x7FFFFFFF);
+    const bool take = (mcur == jm) && (mcur != kNoColumn);
     const unsigned long long m = __ballot(take);
     if (take) {
       out->vidx[lane] = (int)mptr;
@@ -388,320 +352,270 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     const int* src = mptr < mend ? a.col_idx + mptr : &kNoColumn;
     async_copy4(src, reinterpret_cast<char*>(curcol));
     if (lane == 0) { out->j = jm; out->mask = m; }
-    if (paged && jm != 0x7FFFFFFF) {
+    if (paged && jm != kNoColumn) {
       for (int k0 = 0; k0 < B; k0 += 64) {
         const int key = min(jm * B + k0 + lane, ri.klen - 1);
         async_copy4(R.block_table + (size_t)ri.seq * R.max_pages + key / R.page_size,
                     reinterpret_cast<char*>(out->page + k0));
-        ++copies;
       }
     }
-    return copies;
   };
   __syncthreads();
   if (wave == 0) merge(&UI[0]);
   wait_vmcnt<0>();
   __syncthreads();
+  if (wave == 0) merge(&UI[1]);
+  wait_vmcnt<0>();
+  __syncthreads();
 
-  const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
-  const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(R.v) + (size_t)l * R.lsv;
+  f32x16 O[2][C::NT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) O[qt][nt] = f32x16{};
 
-  // P copies: instruction (wave, i) copies head h = wave + i NW, lane L row
-  // e = L / 8 (key 8 si + e of the block), chunk L % 8 from source chunk
-  // (L % 8) ^ swz_p(h).  Sources are prepared once per union block, so a
-  // stage adds one offset.  Heads that do not keep the block issue no copy:
-  // their slot keeps an earlier block's finite values (or the initial
-  // zeros), which meet a zero weight in the head mix.
-  const bf16* pbase[C::PW];
-  unsigned plive = 0;   // bit i: copy slot i of this wave reads a kept block
-  auto prep_p = [&](const UnionInfo* ui) {
-    const unsigned long long mk = ui ? ui->mask : 0ull;
-    const int e = lane >> 3, pc = lane & 7;
-    unsigned bits = 0;
+  if (UI[0].j != kNoColumn) {
+    const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
+    const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(R.v) + (size_t)l * R.lsv;
+
+    // ---- P copies.  Every wave issues PCW copies per stage.  Instruction
+    // (wave, i) copies head pair c = wave + 8 i: lane L writes head
+    // 2c + L / 32, physical key row (L / 8) % 4, chunk L % 8 of the stage,
+    // which hold logical key row ^ gp(h) and query chunk (L % 8) ^ fp(h).
+    // A head that does not keep the block (or does not exist) copies the rows
+    // of its partner, else of the block's first keeping head: finite values
+    // the mix gives zero weight, fetched from L2 by the copy of their owner.
+    const bf16* pbase[C::PCW];
+    auto prep_p = [&](const UnionInfo* ui) {
+      const unsigned long long mk = ui->mask;
+      const int h0 = __builtin_ctzll(mk);
+      const int kp = (lane >> 3) & 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < C::PW; ++i) {
-      const int h = wave + i * C::NW;
-      const int sc = pc ^ swz_p(h);
-      const bool live = h < a.Hs && ((mk >> h) & 1ull);
-      pbase[i] = live ? vals + (size_t)ui->vidx[h] * B * B + (size_t)e * B + qoff + 8 * sc : vals;
-      bits |= live ? 1u << i : 0u;
-    }
-    plive = __builtin_amdgcn_readfirstlane(bits);
-  };
-  auto issue_p = [&](int si, char* buf) {
-#pragma unroll
-    for (int i = 0; i < C::PW; ++i)
-      if ((plive >> i) & 1u)
-        async_copy16(pbase[i] + (size_t)si * 8 * B, buf + (size_t)(wave + i * C::NW) * C::HSTR);
-    return __builtin_popcount(plive);
-  };
-  // Half-stage copies: instruction (wave, i) copies head pair c = wave + i NW,
-  // lane L head 2c + L / 32, row r = (L / 8) % 4, chunk L % 8.  Row r of
-  // head h holds key r ^ (h & 1) of the half-stage (odd heads swap key
-  // pairs, which puts the same key of neighbouring heads in opposite bank
-  // halves), chunk from source chunk (L % 8) ^ swz_p(h).  A pair issues a
-  // copy when either head keeps the block; the lanes of a head that does not
-  // keep it read rows of the first stored block instead (finite values that
-  // meet a zero weight).
-  const bf16* hbase[C::HALF ? C::PWH : 1];
-  unsigned hlive = 0;
-  auto prep_h = [&](const UnionInfo* ui) {
-    const unsigned long long mk = ui ? ui->mask : 0ull;
-    const int r = (lane >> 3) & 3, pc = lane & 7;
-    unsigned bits = 0;
-#pragma unroll
-    for (int i = 0; i < C::PWH; ++i) {
-      const int c = wave + i * C::NW, h = 2 * c + (lane >> 5);
-      const int sc = pc ^ swz_p(h);
-      const bool live = h < a.Hs && ((mk >> h) & 1ull);
-      const bool plv = ((mk >> (2 * c)) & 3ull) != 0ull && 2 * c < a.Hs;
-      hbase[i] = vals + (live ? (size_t)ui->vidx[h] * B * B : (size_t)0) + (size_t)(r ^ (h & 1)) * B + qoff + 8 * sc;
-      bits |= plv ? 1u << i : 0u;
-    }
-    hlive = __builtin_amdgcn_readfirstlane(bits);
-  };
-  auto issue_h = [&](int hsi, char* slot) {
-#pragma unroll
-    for (int i = 0; i < C::PWH; ++i)
-      if ((hlive >> i) & 1u)
-        async_copy16(hbase[i] + (size_t)hsi * 4 * B, slot + (size_t)(wave + i * C::NW) * 1024);
-    return __builtin_popcount(hlive);
-  };
-  // The group's receiver heads read nkv consecutive value heads kv0 ..
-  // kv0 + nkv - 1 (grouped-query attention: ratio receivers per value head).
-  // V rows of the VK-key part hh of the block (16 keys with the stage ring,
-  // 32 with the half-stage ring), staged once per value head -> Vs, row
-  // VK kvl + key
-  const int ratio = R.Hr / R.Hkv;
-  const int kv0 = (8 * grp) / ratio;
-  const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
-  auto issue_v = [&](const UnionInfo* ui, int hh, int buf) {
-    const int ln = opaque(lane);
-    const int ninst = nkv * (C::VK / C::RPI);
-    char* vdst = Vs + (size_t)buf * C::VBUF;
-#pragma unroll 1
-    for (int k = wave; k < ninst; k += C::NW) {
-      const int rho = k * C::RPI + ln / C::VCPR;
-      const int p = ln % C::VCPR;
-      const int kvl = rho / C::VK, cl = rho % C::VK;
-      const int kl = C::VK * hh + cl;                  // key inside the block
-      const int key = ui->j * B + kl;
-      const bool live = key < ri.klen;
-      const int g = kv0 + kvl;
-      const int lc = p ^ swz_v(rho, C::VCPR);
-      size_t tok;
-      if (paged) {
-        int64_t page = live ? ui->page[kl] : 0;
-        page = page < 0 ? 0 : (page >= R.num_pages ? R.num_pages - 1 : page);
-        tok = live ? (size_t)page * R.page_size + key % R.page_size : 0;
-      } else {
-        tok = (size_t)ri.k0 + (live ? key : 0);
+      for (int i = 0; i < C::PCW; ++i) {
+        const int c = wave + kMapWaves * i, h = 2 * c + lh, hp = h ^ 1;
+        const bool mine = h < a.Hs && ((mk >> h) & 1ull);
+        const bool partner = hp < a.Hs && ((mk >> hp) & 1ull);
+        const int e = ui->vidx[mine ? h : (partner ? hp : h0)];
+        pbase[i] = vals + (size_t)e * B * B + (size_t)(kp ^ gp_swz(h)) * B + qoff + 8 * (pc ^ fp_swz(h));
       }
-      async_copy16(vbase + (tok * R.Hkv + g) * D + 8 * lc, vdst + (size_t)k * 1024);
-    }
-    return wave < ninst ? (ninst - 1 - wave) / C::NW + 1 : 0;
-  };
-
-  f32x4 O[4][C::NT];
+    };
+    // issue cursor of the P copies: stage psi of block pu in ring slot pslot;
+    // past the union it issues copies of the last block's first stage into
+    // slots no stage reads again
+    int psi = 0, pslot = 0, prot = 0;
+    bool pdone = false;
+    auto issue_next_p = [&]() {
+      char* slot = ring + (size_t)pslot * C::SLOT;
+      const size_t so = (size_t)(pdone ? 0 : psi) * 4 * B;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) O[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // per-lane transpose-read offsets inside a ring slot: key e of heads
-  // h = 32 hk + 8 lg + (lr >> 2) and h + 4, queries q .. q + 3 (the key adds
-  // e * PROW, an immediate)
-  const int q = 16 * qt + 4 * (lr & 3);
-  const int pch = q >> 3, pwithin = (q & 7) * 2;
-  unsigned moff[2][2];
-#pragma unroll
-  for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int h = 32 * hk + 8 * lg + (lr >> 2) + 4 * t;
-      moff[hk][t] = (unsigned)(h * (C::HALF ? 4 * C::PROW : C::HSTR) + ((pch ^ swz_p(h)) << 4) + pwithin);
-    }
-  const float* wrow = Wsh + (4 * hq + (lr & 3)) * 64;
-  const unsigned ppar = ((lr >> 2) & 1) * C::PROW;     // this lane's heads are odd: key pairs swapped
-
-  if (UI[0].j != 0x7FFFFFFF) {
-    // stages are numbered over the whole walk: stage s is stage s % SPU of
-    // union block s / SPU (half-stage t is half-stage t % HPU of block
-    // t / HPU).  Copies outstanding at the top of a stage:
-    //  - half-stage ring: the prologue issues half-stages 0..2 and stage s
-    //    issues 2s+3 and 2s+4, so only 2s+2, the previous stage's last
-    //    copies, may still be in flight; the V rows of a step (and the
-    //    merge's copies), issued before the P copies of its first stage, have
-    //    landed by its second;
-    //  - stage ring, two V buffers: every copy is needed two stages after
-    //    the one that issued it at the earliest, so all of the previous
-    //    stage's copies may still be in flight;
-    //  - stage ring, one V buffer: the V rows issued at a half's first stage
-    //    (and the merge's copies, issued before them) are needed at its
-    //    second, so only the previous stage's P copies, always its last, may
-    //    be;
-    //  - 2-slot stage ring: everything is waited for.
-    int ops_prev = 0, p_prev = 0;
-    if constexpr (C::HALF) {
-      prep_h(&UI[0]);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) p_prev = issue_h(t, ring + (size_t)t * C::HSB);
-    } else {
-      prep_p(&UI[0]);
-      if (C::NVB == 2) issue_v(&UI[0], 0, 0);
-#pragma unroll
-      for (int t = 0; t < C::AHEAD; ++t) p_prev = issue_p(t, ring + (size_t)t * C::SBYTES);
-    }
-    ops_prev = p_prev;
-    bf16x8 Wk[2];
-    f32x4 Cacc[8];
-#pragma unroll
-    for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0;; ++s) {
-      // P rows of stage s and the V rows of its half have landed (only the
-      // P copies issued at stage s - 1, the wave's latest, may still be in
-      // flight)
-      if (C::HALF) {
-        // half-stages 2s and 2s+1 have landed; only 2s+2, issued last at
-        // stage s-1, may be in flight
-        wait_vmcnt_upto<C::PWH>(p_prev);
-      } else if (C::AHEAD == 1) {
-        wait_vmcnt<0>();
-      } else if (C::NVB == 1) {
-        wait_vmcnt_upto<C::PW>(p_prev);
-      } else {
-        wait_vmcnt_upto<15>(ops_prev);
+      for (int i = 0; i < C::PCW; ++i) async_copy16(pbase[i] + so, slot + (size_t)(wave + kMapWaves * i) * 1024);
+      pslot = pslot + 1 == NS ? 0 : pslot + 1;
+      if (!pdone && ++psi == C::SPB) {
+        psi = 0;
+        prot = prot == kUnionSlots - 1 ? 0 : prot + 1;
+        const UnionInfo* nx = &UI[prot];
+        if (nx->j == kNoColumn) pdone = true;
+        else prep_p(nx);
       }
-      __syncthreads();
-      const int u = s / C::SPU, si = s % C::SPU;
-      const UnionInfo* ui = &UI[u & 1];
-      if (si == 0 && ui->j == 0x7FFFFFFF) break;
-      const int g2 = si & 3;
-      int ops = 0;
-      if (si == 0) {
-        if (wave == 0) ops += merge(&UI[(u + 1) & 1]);
-        // W of this union block: sender heads that do not keep j get weight 0
-        const unsigned long long mk = ui->mask;
+    };
+
+    // ---- V copies.  The group's receiver heads read nkv consecutive value
+    // heads kv0 .. kv0 + nkv - 1 (grouped-query attention: ratio receivers
+    // per value head), staged once per value head.  Row rho = 16 kvl + key of
+    // the buffer holds value head kv0 + kvl at key 16 st + key of the block;
+    // lane L of instruction k writes row k VRPI + L / VCPR, chunk L % VCPR,
+    // which holds d chunk (L % VCPR) ^ sv(key).  Every wave issues VC
+    // copies; rows of value heads past nkv, and every row past the union,
+    // copy the first row (nothing reads them).
+    const int ratio = R.Hr / R.Hkv;
+    const int kv0 = (8 * grp) / ratio;
+    const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
+    auto issue_v = [&](const UnionInfo* ui, int st, char* dst, bool real) {
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-          for (int ee = 0; ee < 8; ++ee) {
-            const int h = 32 * hk + 8 * lg + ee;
-            Wk[hk][ee] = (bf16)(((mk >> h) & 1ull) ? wrow[h] : 0.f);
-          }
-      }
-      // V rows: with two buffers, those of the next half at the last stage of
-      // this one (into the other buffer); with one, those of this half at
-      // its first stage
-      if (C::HALF) {
-        // V rows of this 32-key step, needed at its last stage
-        if (g2 == 0) ops += issue_v(ui, si >> 2, 0);
-      } else if (C::NVB == 2) {
-        if (g2 & 1) {
-          const int s1 = s + 1;
-          const UnionInfo* ui1 = &UI[(s1 / C::SPU) & 1];
-          if (ui1->j != 0x7FFFFFFF) {
-            ops += issue_v(ui1, (s1 % C::SPU) >> 1, (s1 >> 1) & 1);
-          }
+      for (int i = 0; i < C::VC; ++i) {
+        const int k = wave + kMapWaves * i;
+        const int rho = k * C::VRPI + lane / C::VCPR, p = lane % C::VCPR;
+        const int kvl = rho >> 4, kk = rho & 15;
+        const int kl = 16 * st + kk;                     // key inside the block
+        const int key = real ? ui->j * B + kl : 0;
+        const bool live = real && kvl < nkv && key < ri.klen;
+        size_t tok;
+        if (paged) {
+          int64_t page = live ? ui->page[kl] : 0;
+          page = page < 0 ? 0 : (page >= R.num_pages ? R.num_pages - 1 : page);
+          tok = live ? (size_t)page * R.page_size + key % R.page_size : 0;
+        } else {
+          tok = (size_t)ri.k0 + (live ? key : 0);
         }
-      } else if ((g2 & 1) == 0) {
-        ops += issue_v(ui, si >> 1, 0);
+        async_copy16(vbase + (tok * R.Hkv + kv0 + (live ? kvl : 0)) * D + 8 * (p ^ sv_swz<D>(kk)),
+                     dst + (size_t)k * 1024);
       }
-      // ---- P copies of stage s + AHEAD (dummy rows past the last block)
-      if constexpr (C::HALF) {
-        // half-stages 2s+3 and 2s+4, into the slots stage s-1 consumed
-#pragma unroll
-        for (int k = 3; k <= 4; ++k) {
-          const int t = 2 * s + k, u2 = t / C::HPU, hsi = t % C::HPU;
-          if (hsi == 0) {
-            const UnionInfo* ui2 = &UI[u2 & 1];
-            prep_h(ui2->j != 0x7FFFFFFF ? ui2 : nullptr);
-          }
-          p_prev = issue_h(hsi, ring + (size_t)(t % C::NHS) * C::HSB);
-          ops += p_prev;
-        }
-      } else {
-        const int s2 = s + C::AHEAD, u2 = s2 / C::SPU, si2 = s2 % C::SPU;
-        if (si2 == 0) {
-          const UnionInfo* ui2 = &UI[u2 & 1];
-          prep_p(ui2->j != 0x7FFFFFFF ? ui2 : nullptr);
-        }
-        p_prev = issue_p(si2, ring + (size_t)(s2 % C::NSLOT) * C::SBYTES);
-        ops += p_prev;
-      }
-      ops_prev = ops;
+    };
 
-      // ---- head mix over the 8 keys of key group g2: lanes of key group g2
-      // take W, the others zero (block-diagonal)
-      const char* cur = ring + (size_t)(s % C::NSLOT) * C::SBYTES;
-      const char* curA = ring + (size_t)((2 * s) % C::NHS) * C::HSB;
-      const char* curB = ring + (size_t)((2 * s + 1) % C::NHS) * C::HSB;
-      const bf16x8 zero8 = {};
+    // ---- this wave's roles
+    // mix: key mkey of each stage, queries mq0 .. mq0 + 31; per-lane
+    // transposing-read offsets inside a ring slot for (chunk kc, head quad
+    // hh, query tile qi), and whether the quad is staged (HP is a multiple
+    // of 16, so a 16-lane group's four heads are all staged or all not)
+    const int mkey = wave >> 1;
+    const int mq0 = 32 * (wave & 1);
+    unsigned moff[C::NKC][2][2];
+    bool mstaged[C::NKC][2];
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        if (32 * hk < hpad) {
-          const bf16x8 wop = ((lr >> 2) == g2) ? Wk[hk] : zero8;
-          const bool hv = 32 * hk + 8 * lg < hpad;
-          // A transposing read gives each lane data from rows other lanes
-          // address, so it never runs under a partial exec mask: every lane
-          // reads (lanes past the padded heads at head 0's rows) and the
-          // lanes past the heads take zeros afterwards.
-          const unsigned o0 = hv ? moff[hk][0] : moff[0][0];
-          const unsigned o1 = hv ? moff[hk][1] : moff[0][1];
-          // all eight operands first, then the MFMAs
-          bf16x8 pop[8];
+    for (int kc = 0; kc < C::NKC; ++kc)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            bf16x4 lo, hi;
-            if constexpr (C::HALF) {
-              const char* hs = e < 4 ? curA : curB;
-              const int ep = e & 3;
-              const unsigned kofs = (ep & 1) ? (ep - 1) * C::PROW + (C::PROW - ppar) : ep * C::PROW + ppar;
-              lo = tr_read(hs, o0 + kofs);
-              hi = tr_read(hs, o1 + kofs);
-            } else {
-              lo = tr_read(cur, o0 + e * C::PROW);
-              hi = tr_read(cur, o1 + e * C::PROW);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h0 = 32 * kc + 8 * lg + 4 * hh;
+        mstaged[kc][hh] = h0 < HP;
+        const int h = (h0 < HP ? h0 : 0) + (l16 >> 2);
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          const int q = mq0 + 16 * qi + 4 * (l16 & 3);
+          moff[kc][hh][qi] = (unsigned)(h * 4 * C::PROW + (mkey ^ gp_swz(h)) * C::PROW + (((q >> 3) ^ fp_swz(h)) << 4) +
+                                        (q & 7) * 2);
+        }
+      }
+    // P.V: receiver head 8 grp + wave, its value head in the V buffer
+    const int kvl = min((8 * grp + wave) / ratio - kv0, KVC - 1);
+    const char* asrc = abuf + (size_t)wave * C::AHS;
+    unsigned aoff[2][2];   // A operand reads (query tile, key half)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = 8 * lh + 4 * hh + (l16 >> 2);
+        const int q = 32 * qt + 16 * (lg & 1) + 4 * (l16 & 3);
+        aoff[qt][hh] = (unsigned)(key * C::PROW + (((q >> 3) ^ sa_swz(key)) << 4) + (q & 7) * 2);
+      }
+    unsigned voff[C::NT][2];
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = 8 * lh + 4 * hh + (l16 >> 2);
+        const int n = 32 * nt + 16 * (lg & 1) + 4 * (l16 & 3);
+        voff[nt][hh] = (unsigned)((kvl * 16 + key) * C::VROW + (((n >> 3) ^ sv_swz<D>(key)) << 4) + (n & 7) * 2);
+      }
+
+    // W of the current block as the mix's B operand: lane L supplies receiver
+    // head L % 16 (zero past the group's 8 and past Hr) and sender heads
+    // 32 kc + 8 (L / 16) + e; heads that do not keep the block (or do not
+    // exist) weigh 0
+    bf16x8 Wk[C::NKC];
+    auto prep_w = [&](const UnionInfo* ui) {
+      const unsigned long long mk = ui->mask;
+      const bool rok = l16 < 8;
+      const float* wrow = Wsh + (rok ? l16 : 0) * 64;
+#pragma unroll
+      for (int kc = 0; kc < C::NKC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int h = 32 * kc + 8 * lg + e;
+          Wk[kc][e] = (bf16)((rok && h < 64 && ((mk >> h) & 1ull)) ? wrow[h] : 0.f);
+        }
+    };
+
+    prep_p(&UI[0]);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) issue_next_p();
+
+    bf16x8 Aop[2];
+    int st = 0, crot = 0, mslot = 0;      // step in block, UI slot of its block, ring slot being mixed
+    bool mixing = true, pvv = false;      // this step mixes; the previous one did (its P.V runs now)
+    for (int T = 0;; ++T) {
+      // one 16-key step: four stages p = 0..3 with compile-time roles
+      auto stage = [&](auto PP) -> bool {
+        constexpr int p = decltype(PP)::value;
+        // the wave's copies of this stage and everything older have landed
+        wait_vmcnt<C::allow(p)>();
+        __syncthreads();
+        if constexpr (p == 0) {
+          if (mixing && st == 0 && UI[crot].j == kNoColumn) mixing = false;
+          if (!mixing && !pvv) return false;
+          if (pvv) {
+            // the previous step's mixed map as P.V operands: lane L gets
+            // queries 32 qt + L % 32, keys 8 (L / 32) + 0..7
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+              const bf16x4 lo = tr_read(asrc, aoff[qt][0]);
+              const bf16x4 hi = tr_read(asrc, aoff[qt][1]);
+              Aop[qt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            const bf16x8 pv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            pop[e] = hv ? pv : zero8;
           }
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            Cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, pop[e], Cacc[e], 0, 0, 0);
+          // every wave holds its operands before this step's mix overwrites them
+          __syncthreads();
+          if (mixing && st == 0) prep_w(&UI[crot]);
         }
-      }
-      if (C::HALF ? g2 == 3 : (g2 & 1) != 0) {
-        // ---- P.V over the 16 keys of this half: A_r[q][32cb + 8lg + e] =
-        // Cacc[e][i]; lane groups of the other half hold zeros, and their V
-        // rows (any finite row of the buffer) add nothing
-        bf16x8 Aop[4];
+        // copies: the step's V rows, the union two blocks ahead, P of the
+        // stage NS - 1 ahead
+        if constexpr (p == C::VPART)
+          issue_v(&UI[crot], st, vbuf + (size_t)(NVB == 2 ? (T & 1) : 0) * C::VB, mixing);
+        if constexpr (p == 1)
+          if (mixing && st == 0 && wave == 0) merge(&UI[crot == 0 ? 2 : crot - 1]);
+        issue_next_p();
+
+        // ---- head mix of this stage: key mkey, queries mq0 .. mq0 + 31
+        if (mixing) {
+          const char* slot = ring + (size_t)mslot * C::SLOT;
+          constexpr int kb = 4 * p;                       // first key of the stage inside the step
+          const int akey = kb + mkey;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int qi = 0; qi < 2; ++qi) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ee = 0; ee < 8; ++ee) Aop[i][ee] = (bf16)Cacc[ee][i];
-        const int nlo = 4 * (lr & 3);
-        const char* Vh = Vs + (size_t)(!C::HALF && C::NVB == 2 ? (s >> 1) & 1 : 0) * C::VBUF;
+            for (int kc = 0; kc < C::NKC; ++kc) {
+              bf16x4 part[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // value head of receiver 8 grp + 4 hq + i, local to the group (a
-          // padding receiver past Hr reads some staged row: its mixed map is 0)
-          const int kvl = min((8 * grp + 4 * hq + i) / ratio - kv0, KVC - 1);
-          const int rho0 = kvl * C::VK + 8 * (C::HALF ? lg : (lg & 1)) + (lr >> 2);
-          const int sw0 = swz_v(rho0, C::VCPR);         // same for rho0 + 4
+              for (int hh = 0; hh < 2; ++hh) {
+                // a transposing read hands each lane values from rows other
+                // lanes of its 16-lane group address, so it never runs under
+                // a partial exec mask: unstaged quads read heads 0..3 and
+                // take a zero operand
+                const bf16x4 v = tr_read(slot, moff[kc][hh][qi]);
+                part[hh] = mstaged[kc][hh] ? v : bf16x4{};
+              }
+              const bf16x8 op = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, Wk[kc], acc, 0, 0, 0);
+            }
+            // lane (lg, r): queries mq0 + 16 qi + 4 lg + i of receiver head r
+            if (l16 < 8) {
+              const int qq = mq0 + 16 * qi + 4 * lg;
+              bf16x4 o4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o4[i] = (bf16)acc[i];
+              const unsigned off = (unsigned)(l16 * C::AHS + akey * C::PROW + (((qq >> 3) ^ sa_swz(akey)) << 4) +
+                                              (qq & 7) * 2);
+              *reinterpret_cast<bf16x4*>(abuf + off) = o4;
+            }
+          }
+        }
+        mslot = mslot + 1 == NS ? 0 : mslot + 1;
+
+        // ---- P.V of the previous step: one 32-wide n tile per stage (two
+        // V buffers) or all of d at the first stage (one buffer)
+        if (pvv) {
+          const char* vsrc = vbuf + (size_t)(NVB == 2 ? ((T - 1) & 1) : 0) * C::VB;
 #pragma unroll
           for (int nt = 0; nt < C::NT; ++nt) {
-            const int n = 16 * nt + nlo;
-            const int lc = n >> 3, within = (n & 7) * 2;
-            const unsigned off = (unsigned)(rho0 * C::VROW + ((lc ^ sw0) << 4) + within);
-            const bf16x4 lo = tr_read(Vh, off);
-            const bf16x4 hi = tr_read(Vh, off + 4 * C::VROW);
+            if (NVB == 2 ? nt != p : p != 0) continue;
+            const bf16x4 lo = tr_read(vsrc, voff[nt][0]);
+            const bf16x4 hi = tr_read(vsrc, voff[nt][1]);
             const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            O[i][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop[i], vop, O[i][nt], 0, 0, 0);
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+              O[qt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aop[qt], vop, O[qt][nt], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int ee = 0; ee < 8; ++ee) Cacc[ee] = f32x4{0.f, 0.f, 0.f, 0.f};
+        return true;
+      };
+      if (!stage(IC<0>{})) break;
+      stage(IC<1>{});
+      stage(IC<2>{});
+      stage(IC<3>{});
+      pvv = mixing;
+      if (mixing && ++st == C::SB) {
+        st = 0;
+        crot = crot == kUnionSlots - 1 ? 0 : crot + 1;
       }
     }
   }
@@ -711,19 +625,19 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   __syncthreads();
   bf16* stage = reinterpret_cast<bf16*>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int qq = 16 * qt + 4 * lg + ii;
-        stage[((size_t)qq * 8 + 4 * hq + i) * D + 16 * nt + lr] = (bf16)O[i][nt][ii];
+      for (int i = 0; i < 16; ++i) {
+        const int qq = 32 * qt + 8 * (i >> 2) + 4 * lh + (i & 3);
+        stage[((size_t)qq * 8 + wave) * D + 32 * nt + (lane & 31)] = (bf16)O[qt][nt][i];
       }
   __syncthreads();
   bf16* __restrict__ obase = reinterpret_cast<bf16*>(R.o) + (size_t)l * R.lso;
   const int heads_here = min(8, R.Hr - 8 * grp);
   constexpr int CPQ = 8 * D * 2 / 16;                  // 16-byte chunks per query row
-  for (int c = tid; c < C::RQ * CPQ; c += C::NW * 64) {
+  for (int c = tid; c < kMapRows * CPQ; c += kMapWaves * 64) {
     const int qq = c / CPQ, k = c % CPQ;
     const int hl = (k * 8) / D;
     if (qoff + qq < ri.rows && hl < heads_here) {
@@ -736,32 +650,55 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   }
 }
 
-template <int B, int D, int HP8, int KVC>
-int launch_fast_h(const MappedArgs& a, void* stream) {
-  using C = MapCfg<B, D, HP8, KVC>;
-  const size_t lds = mapped_mfma_lds_bytes(B, D, a.Hs, KVC);
-  auto kern = mapped_mfma_kernel<B, D, HP8, KVC>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+// Largest ring / V-buffer plan whose LDS fits, preferring a 4-slot ring with
+// two V buffers.  Returns false if none fits.
+bool map_plan(int B, int D, int HP, int KVC, size_t lds_limit, int* ns, int* nvb) {
+  static const int plans[][2] = {{4, 2}, {4, 1}, {3, 2}, {3, 1}, {2, 1}};
+  for (const auto& p : plans)
+    if (map_lds_bytes(B, D, HP, KVC, p[0], p[1]) <= lds_limit) {
+      *ns = p[0];
+      *nvb = p[1];
+      return true;
+    }
+  return false;
+}
+
+template <int B, int D, int HP, int KVC, int NS, int NVB>
+int launch_fast_cfg(const MappedArgs& a, void* stream) {
+  using C = MapCfg<B, D, HP, KVC, NS, NVB>;
+  // plans past the 160 KB of LDS are never chosen (map_plan); none is built
+  if constexpr (C::LDS > 163840) {
+    return (int)hipErrorInvalidValue;
+  } else {
+  auto kern = mapped_mfma_kernel<B, D, HP, KVC, NS, NVB>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
   if (e != hipSuccess) return (int)e;
   int ngroups = 0;
   for (int k = 0; k < a.nrecv; ++k) ngroups += (a.rx[k].Hr + 7) / 8;
   const long long nu = (long long)a.b.total_rb * C::QH * a.L;
   const long long per_xcd = (nu + kXcds - 1) / kXcds * ngroups;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::NW * 64), lds, (hipStream_t)stream, a, ngroups);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(kMapWaves * 64), C::LDS, (hipStream_t)stream,
+                     a, ngroups);
   return (int)hipGetLastError();
+  }
+}
+
+template <int B, int D, int HP, int KVC>
+int launch_fast_p(const MappedArgs& a, void* stream, int ns, int nvb) {
+  if (ns == 4 && nvb == 2) return launch_fast_cfg<B, D, HP, KVC, 4, 2>(a, stream);
+  if (ns == 4 && nvb == 1) return launch_fast_cfg<B, D, HP, KVC, 4, 1>(a, stream);
+  if (ns == 3 && nvb == 2) return launch_fast_cfg<B, D, HP, KVC, 3, 2>(a, stream);
+  if (ns == 3 && nvb == 1) return launch_fast_cfg<B, D, HP, KVC, 3, 1>(a, stream);
+  return launch_fast_cfg<B, D, HP, KVC, 2, 1>(a, stream);
 }
 
 template <int B, int D, int KVC>
-int launch_fast_k(const MappedArgs& a, void* stream) {
-  switch ((a.Hs + 7) / 8) {
-    case 1: return launch_fast_h<B, D, 1, KVC>(a, stream);
-    case 2: return launch_fast_h<B, D, 2, KVC>(a, stream);
-    case 3: return launch_fast_h<B, D, 3, KVC>(a, stream);
-    case 4: return launch_fast_h<B, D, 4, KVC>(a, stream);
-    case 5: return launch_fast_h<B, D, 5, KVC>(a, stream);
-    case 6: return launch_fast_h<B, D, 6, KVC>(a, stream);
-    case 7: return launch_fast_h<B, D, 7, KVC>(a, stream);
-    case 8: return launch_fast_h<B, D, 8, KVC>(a, stream);
+int launch_fast_k(const MappedArgs& a, void* stream, int ns, int nvb) {
+  switch ((a.Hs + 15) / 16) {
+    case 1: return launch_fast_p<B, D, 16, KVC>(a, stream, ns, nvb);
+    case 2: return launch_fast_p<B, D, 32, KVC>(a, stream, ns, nvb);
+    case 3: return launch_fast_p<B, D, 48, KVC>(a, stream, ns, nvb);
+    case 4: return launch_fast_p<B, D, 64, KVC>(a, stream, ns, nvb);
   }
   return (int)hipErrorInvalidValue;
 }
@@ -778,8 +715,8 @@ static int max_group_value_heads(const MappedArgs& a) {
 }
 
 template <int B, int D>
-int launch_fast(const MappedArgs& a, void* stream) {
-  return max_group_value_heads(a) <= 4 ? launch_fast_k<B, D, 4>(a, stream) : launch_fast_k<B, D, 8>(a, stream);
+int launch_fast(const MappedArgs& a, void* stream, int kvc, int ns, int nvb) {
+  return kvc <= 4 ? launch_fast_k<B, D, 4>(a, stream, ns, nvb) : launch_fast_k<B, D, 8>(a, stream, ns, nvb);
 }
 
 template <typename T, int B, int D>
@@ -804,18 +741,24 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 }  // namespace
 
-bool mapped_mfma_covers(int B, int d, int Hs, int kv_heads_per_group, size_t lds_limit) {
-  return mapped_mfma_lds_bytes(B, d, Hs, kv_heads_per_group <= 4 ? 4 : 8) <= lds_limit;
+// The MFMA kernel's plan for these shapes (false: the portable kernel runs)
+static bool mapped_mfma_plan(const MappedArgs& a, mf_dtype dt, bool allow_fast, size_t lds_limit, int* kvc, int* ns,
+                             int* nvb) {
+  if (dt != MF_BF16 || !allow_fast || (a.B != 64 && a.B != 128) || (a.d != 64 && a.d != 128)) return false;
+  *kvc = max_group_value_heads(a) <= 4 ? 4 : 8;
+  const int hp = (a.Hs + 15) / 16 * 16;
+  return map_plan(a.B, a.d, hp, *kvc, lds_limit, ns, nvb);
 }
 
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, max_group_value_heads(a), lds_limit)) {
+  int kvc = 0, ns = 0, nvb = 0;
+  if (mapped_mfma_plan(a, dt, allow_fast, lds_limit, &kvc, &ns, &nvb)) {
     switch (a.B * 1000 + a.d) {
-      case 64064: return launch_fast<64, 64>(a, stream);
-      case 64128: return launch_fast<64, 128>(a, stream);
-      case 128064: return launch_fast<128, 64>(a, stream);
-      case 128128: return launch_fast<128, 128>(a, stream);
+      case 64064: return launch_fast<64, 64>(a, stream, kvc, ns, nvb);
+      case 64128: return launch_fast<64, 128>(a, stream, kvc, ns, nvb);
+      case 128064: return launch_fast<128, 64>(a, stream, kvc, ns, nvb);
+      case 128128: return launch_fast<128, 128>(a, stream, kvc, ns, nvb);
     }
   }
   return dt == MF_BF16 ? launch_gd<bf16>(a, stream) : launch_gd<float>(a, stream);
@@ -823,8 +766,8 @@ int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fas
 
 int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
-  if (dt == MF_BF16 && allow_fast && mapped_mfma_covers(a.B, a.d, a.Hs, max_group_value_heads(a), lds_limit) &&
-      (a.B == 64 || a.B == 128) && (a.d == 64 || a.d == 128))
+  int kvc = 0, ns = 0, nvb = 0;
+  if (mapped_mfma_plan(a, dt, allow_fast, lds_limit, &kvc, &ns, &nvb))
     return launch_mapped(a, dt, stream, allow_fast, lds_limit);
   // one launch per receiver
   for (int k = 0; k < a.nrecv; ++k) {

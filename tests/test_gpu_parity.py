@@ -191,7 +191,10 @@ def test_repeat_calls_are_deterministic():
                                             (64, 128, 31, 8, None), (128, 128, 32, 16, None),
                                             # grouped-query receivers: V staged per value head
                                             (64, 128, 32, 24, 8), (128, 128, 40, 32, 8), (64, 64, 24, 12, 4),
-                                            (64, 128, 16, 16, 2), (128, 64, 8, 20, 5), (64, 128, 48, 16, 4)])
+                                            (64, 128, 16, 16, 2), (128, 64, 8, 20, 5), (64, 128, 48, 16, 4),
+                                            # 33-64 sender heads: two K chunks of 32, or 32 + 16
+                                            (64, 64, 64, 8, None), (64, 128, 56, 8, 2), (128, 128, 48, 24, None),
+                                            (128, 64, 36, 16, 8)])
 def test_portable_and_mfma_mapped_kernels_agree_with_oracle(B, d, Hs, Hr, Hkv):
     wl = tiny_structured("bf16", workload_id=14, B=B, d=d, H_s=Hs, H_r=Hr, H_kv_r=Hkv,
                          seqlens=(4 * B + 9, B + 3), num_layers=1)
