@@ -290,7 +290,8 @@ mf_status check_receiver(const mf_receiver_desc* desc, const mf_batch* batch, co
   return MF_OK;
 }
 
-mf::MappedRecv receiver_args(const mf_receiver_desc* desc, const float* W, const void* v, void* o, int group0) {
+mf::MappedRecv receiver_args(const mf_receiver_desc* desc, const mf_batch* batch, const float* W, const void* v,
+                             void* o, int group0) {
   mf::MappedRecv r;
   memset(&r, 0, sizeof(r));
   r.W = W; r.v = v; r.o = o;
@@ -299,6 +300,7 @@ mf::MappedRecv receiver_args(const mf_receiver_desc* desc, const float* W, const
   r.num_pages = desc->num_pages;
   r.Hr = desc->H_r; r.Hkv = desc->H_kv_r;
   r.group0 = group0;
+  r.vrows = desc->block_table ? desc->num_pages * desc->page_size : (int64_t)batch->info.total_k;
   return r;
 }
 
@@ -316,7 +318,7 @@ mf::MappedArgs mapped_args(const mf_receiver_desc* desc, const mf_batch* batch, 
   a.d = desc->d; a.B = desc->B;
   for (int l = 0; l < desc->num_layers; ++l) a.layer_map[l] = desc->layer_map[l];
   a.nrecv = 1;
-  a.rx[0] = receiver_args(desc, W, v, o, 0);
+  a.rx[0] = receiver_args(desc, batch, W, v, o, 0);
   return a;
 }
 
@@ -366,7 +368,7 @@ mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_rec
   mf::MappedArgs a = mapped_args(d0, batch, row_ptr, col_idx, values, W[0], v[0], o[0]);
   int groups = 0;
   for (int k = 0; k < n_receivers; ++k) {
-    a.rx[k] = receiver_args(descs[k], W[k], v[k], o[k], groups);
+    a.rx[k] = receiver_args(descs[k], batch, W[k], v[k], o[k], groups);
     groups += (descs[k]->H_r + 7) / 8;
   }
   a.nrecv = n_receivers;

@@ -85,6 +85,7 @@ struct MappedRecv {
   int64_t num_pages;
   int32_t Hr, Hkv;
   int32_t group0;
+  int64_t vrows;           // value rows of one layer (tokens, or pages x page size)
 };
 
 struct MappedArgs {

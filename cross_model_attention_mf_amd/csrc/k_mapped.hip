@@ -180,6 +180,63 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// N copies of 16 bytes per lane whose LDS destinations lie 8 KB apart (one
+// M0 write, then increments).  P: a 64-bit address per copy.  V: one 32-bit
+// lane offset against a per-copy scalar base.
+template <int N>
+__device__ __forceinline__ void copy_p(const bf16* const (&src)[N], unsigned m0);
+template <>
+__device__ __forceinline__ void copy_p<1>(const bf16* const (&src)[1], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src[0]), "s"(m0)
+               : "memory", "m0");
+}
+template <>
+__device__ __forceinline__ void copy_p<2>(const bf16* const (&src)[2], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               : : "v"(src[0]), "v"(src[1]), "s"(m0) : "memory", "m0", "scc");
+}
+template <>
+__device__ __forceinline__ void copy_p<3>(const bf16* const (&src)[3], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off"
+               : : "v"(src[0]), "v"(src[1]), "v"(src[2]), "s"(m0) : "memory", "m0", "scc");
+}
+template <>
+__device__ __forceinline__ void copy_p<4>(const bf16* const (&src)[4], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, off"
+               : : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "s"(m0) : "memory", "m0", "scc");
+}
+template <int N>
+__device__ __forceinline__ void copy_v(unsigned voff, const char* const (&base)[N], unsigned m0);
+template <>
+__device__ __forceinline__ void copy_v<1>(unsigned voff, const char* const (&base)[1], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base[0]), "s"(m0)
+               : "memory", "m0");
+}
+template <>
+__device__ __forceinline__ void copy_v<2>(unsigned voff, const char* const (&base)[2], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+               : : "v"(voff), "s"(base[0]), "s"(base[1]), "s"(m0) : "memory", "m0", "scc");
+}
+template <>
+__device__ __forceinline__ void copy_v<4>(unsigned voff, const char* const (&base)[4], unsigned m0) {
+  asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %3\n\t"
+               "s_add_u32 m0, m0, 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
+               : : "v"(voff), "s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]), "s"(m0)
+               : "memory", "m0", "scc");
+}
+__device__ __forceinline__ unsigned lds_addr(const char* lds_generic) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic);
+}
+
 // chunk / row swizzles (see above)
 __host__ __device__ constexpr int fp_swz(int h) { return 2 * ((h & 1) | (((h >> 3) & 1) << 1)); }
 __host__ __device__ constexpr int gp_swz(int h) { return (h >> 1) & 1; }
@@ -218,11 +275,15 @@ struct MapCfg {
   static constexpr int VRPI = 1024 / VROW;           // V rows per copy instruction
   static constexpr int VB = KVC * 16 * VROW;         // V rows of one 16-key step
   static constexpr int VC = KVC * 16 / VRPI / kMapWaves;   // V copy instructions per wave and step
-  static constexpr int AHS = 16 * PROW + 32;         // mixed map of one receiver head, padded
+  static constexpr int AHS = 12 * PROW + 32;         // mixed map, keys 4..15 of a step, per receiver head
   static constexpr int AB = 8 * AHS;
+  static constexpr int SHS = 8 * PROW + 32;          // keys 0..3 of a step, two step parities, per receiver head
+  static constexpr int SB2 = 8 * SHS;
   static constexpr int VOFF = NS * SLOT;
   static constexpr int AOFF = VOFF + NVB * VB;
-  static constexpr int MAIN = AOFF + AB;
+  static constexpr int SOFF = AOFF + AB;
+  static constexpr int DOFF = SOFF + SB2;            // writes nothing reads: padded mix lanes, dummy copies
+  static constexpr int MAIN = DOFF + 2048;
   static constexpr int OST = kMapRows * 8 * D * 2;   // output staging (aliases the buffers above)
   static constexpr int MAINX = ((MAIN > OST ? MAIN : OST) + 15) / 16 * 16;
   static constexpr size_t LDS = (size_t)MAINX + kMapMeta;
@@ -231,10 +292,13 @@ struct MapCfg {
   static constexpr int NT = D / 32;                  // 32-wide n tiles of d
   static constexpr int VPART = NVB == 2 ? 0 : 1;     // stage of a step that issues the step's V rows
   static_assert(16 % VRPI == 0 && VC * VRPI * kMapWaves == KVC * 16, "V rows fill whole copy instructions");
-  // copies one wave issues at stage p of a step (P copies and V rows), and
-  // how many may still be in flight when stage p opens: those of the NS - 2
-  // stages issued after the copies of stage p
-  static constexpr int ops(int p) { return PCW + (p == VPART ? VC : 0); }
+  // copies one wave issues at stage p of a step (P copies, V rows, and the
+  // union merge's copies, real on wave 0 at a block's first step and dummies
+  // otherwise, so that every wave issues the same count), and how many may
+  // still be in flight when stage p opens: those of the NS - 2 stages issued
+  // after the copies of stage p
+  static constexpr int MC = 1 + B / 64;              // union-merge copies (next columns, page ids)
+  static constexpr int ops(int p) { return PCW + (p == VPART ? VC : 0) + (p == 1 ? MC : 0); }
   static constexpr int allow(int p) {
     int n = 0;
     for (int b = 1; b <= NS - 2; ++b) n += ops((p - b + 8) & 3);
@@ -244,8 +308,8 @@ struct MapCfg {
 
 size_t map_lds_bytes(int B, int D, int HP, int KVC, int NS, int NVB) {
   const size_t prow = 128, slot = (size_t)HP * 4 * prow, vb = (size_t)KVC * 16 * D * 2;
-  const size_t ab = 8 * (16 * prow + 32);
-  const size_t main = NS * slot + NVB * vb + ab;
+  const size_t ab = 8 * (12 * prow + 32), sb = 8 * (8 * prow + 32);
+  const size_t main = NS * slot + NVB * vb + ab + sb + 2048;
   const size_t ost = (size_t)kMapRows * 8 * D * 2;
   const size_t mainx = ((main > ost ? main : ost) + 15) / 16 * 16;
   (void)B;
@@ -278,7 +342,6 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   extern __shared__ __align__(16) char smem[];
   char* const ring = smem;
   char* const vbuf = smem + C::VOFF;
-  char* const abuf = smem + C::AOFF;
   UnionInfo* UI = reinterpret_cast<UnionInfo*>(smem + C::MAINX);
   int* curcol = reinterpret_cast<int*>(UI + kUnionSlots);   // next column of each sender head
   float* Wsh = reinterpret_cast<float*>(curcol + 64);        // [8 receiver heads][64 sender heads]
@@ -352,13 +415,18 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     const int* src = mptr < mend ? a.col_idx + mptr : &kNoColumn;
     async_copy4(src, reinterpret_cast<char*>(curcol));
     if (lane == 0) { out->j = jm; out->mask = m; }
-    if (paged && jm != kNoColumn) {
-      for (int k0 = 0; k0 < B; k0 += 64) {
-        const int key = min(jm * B + k0 + lane, ri.klen - 1);
-        async_copy4(R.block_table + (size_t)ri.seq * R.max_pages + key / R.page_size,
-                    reinterpret_cast<char*>(out->page + k0));
-      }
+    // always B / 64 page copies (dummies when unpaged), so the count is fixed
+    const bool pg = paged && jm != kNoColumn;
+    for (int k0 = 0; k0 < B; k0 += 64) {
+      const int key = pg ? min(jm * B + k0 + lane, ri.klen - 1) : 0;
+      async_copy4(pg ? R.block_table + (size_t)ri.seq * R.max_pages + key / R.page_size : &kNoColumn,
+                  pg ? reinterpret_cast<char*>(out->page + k0) : smem + C::DOFF);
     }
+  };
+  // the same number of copies, into the dump area
+  auto merge_dummy = [&]() {
+#pragma unroll
+    for (int c = 0; c < C::MC; ++c) async_copy4(&kNoColumn, smem + C::DOFF);
   };
   __syncthreads();
   if (wave == 0) merge(&UI[0]);
@@ -376,7 +444,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 
   if (UI[0].j != kNoColumn) {
     const bf16* __restrict__ vals = reinterpret_cast<const bf16*>(a.values);
-    const bf16* __restrict__ vbase = reinterpret_cast<const bf16*>(R.v) + (size_t)l * R.lsv;
+    const char* __restrict__ vlayer = reinterpret_cast<const char*>(R.v) + (size_t)l * R.lsv * 2;
 
     // ---- P copies.  Every wave issues PCW copies per stage.  Instruction
     // (wave, i) copies head pair c = wave + 8 i: lane L writes head
@@ -385,37 +453,51 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     // A head that does not keep the block (or does not exist) copies the rows
     // of its partner, else of the block's first keeping head: finite values
     // the mix gives zero weight, fetched from L2 by the copy of their owner.
-    const bf16* pbase[C::PCW];
-    auto prep_p = [&](const UnionInfo* ui) {
-      const unsigned long long mk = ui->mask;
-      const int h0 = __builtin_ctzll(mk);
+    const bf16* pcur[C::PCW];      // source of each instruction's next copy
+    unsigned pconst[C::PCW];       // the lane's element offset inside a kept block
+    {
       const int kp = (lane >> 3) & 3, pc = lane & 7;
 #pragma unroll
       for (int i = 0; i < C::PCW; ++i) {
-        const int c = wave + kMapWaves * i, h = 2 * c + lh, hp = h ^ 1;
+        const int h = 2 * (wave + kMapWaves * i) + lh;
+        pconst[i] = (unsigned)((kp ^ gp_swz(h)) * B + qoff + 8 * (pc ^ fp_swz(h)));
+      }
+    }
+    auto prep_p = [&](const UnionInfo* ui) {
+      const unsigned long long mk = ui->mask;
+      const int h0 = __builtin_ctzll(mk);
+#pragma unroll
+      for (int i = 0; i < C::PCW; ++i) {
+        const int h = 2 * (wave + kMapWaves * i) + lh, hp = h ^ 1;
         const bool mine = h < a.Hs && ((mk >> h) & 1ull);
         const bool partner = hp < a.Hs && ((mk >> hp) & 1ull);
         const int e = ui->vidx[mine ? h : (partner ? hp : h0)];
-        pbase[i] = vals + (size_t)e * B * B + (size_t)(kp ^ gp_swz(h)) * B + qoff + 8 * (pc ^ fp_swz(h));
+        pcur[i] = vals + (size_t)e * B * B + pconst[i];
       }
     };
-    // issue cursor of the P copies: stage psi of block pu in ring slot pslot;
-    // past the union it issues copies of the last block's first stage into
-    // slots no stage reads again
-    int psi = 0, pslot = 0, prot = 0;
+    // issue cursor: stage psi of the block in union slot prot.  Past the
+    // union it keeps copying the last block's first stage into slots no stage
+    // reads again.
+    int psi = 0, prot = 0;
     bool pdone = false;
-    auto issue_next_p = [&]() {
-      char* slot = ring + (size_t)pslot * C::SLOT;
-      const size_t so = (size_t)(pdone ? 0 : psi) * 4 * B;
+    auto issue_p = [&](int slot) {
+      copy_p<C::PCW>(pcur, lds_addr(ring + (size_t)slot * C::SLOT + (size_t)wave * 1024));
+      if (!pdone) {
+        if (++psi < C::SPB) {
 #pragma unroll
-      for (int i = 0; i < C::PCW; ++i) async_copy16(pbase[i] + so, slot + (size_t)(wave + kMapWaves * i) * 1024);
-      pslot = pslot + 1 == NS ? 0 : pslot + 1;
-      if (!pdone && ++psi == C::SPB) {
-        psi = 0;
-        prot = prot == kUnionSlots - 1 ? 0 : prot + 1;
-        const UnionInfo* nx = &UI[prot];
-        if (nx->j == kNoColumn) pdone = true;
-        else prep_p(nx);
+          for (int i = 0; i < C::PCW; ++i) pcur[i] += 4 * B;
+        } else {
+          psi = 0;
+          prot = prot == kUnionSlots - 1 ? 0 : prot + 1;
+          const UnionInfo* nx = &UI[prot];
+          if (__builtin_amdgcn_readfirstlane(nx->j) == kNoColumn) {
+            pdone = true;
+#pragma unroll
+            for (int i = 0; i < C::PCW; ++i) pcur[i] -= (C::SPB - 1) * 4 * B;
+          } else {
+            prep_p(nx);
+          }
+        }
       }
     };
 
@@ -423,33 +505,41 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     // heads kv0 .. kv0 + nkv - 1 (grouped-query attention: ratio receivers
     // per value head), staged once per value head.  Row rho = 16 kvl + key of
     // the buffer holds value head kv0 + kvl at key 16 st + key of the block;
-    // lane L of instruction k writes row k VRPI + L / VCPR, chunk L % VCPR,
-    // which holds d chunk (L % VCPR) ^ sv(key).  Every wave issues VC
-    // copies; rows of value heads past nkv, and every row past the union,
-    // copy the first row (nothing reads them).
+    // lane L of instruction k = wave + 8 i writes row k VRPI + L / VCPR, chunk
+    // L % VCPR, which holds d chunk (L % VCPR) ^ sv(key).  A lane's key is the
+    // same for every i and the value head steps by KVS, so one lane offset
+    // (its token's row) serves every instruction against a scalar base per
+    // value head.  Value heads past nkv copy head nkv - 1, and keys past the
+    // sequence the sequence's last key: valid rows that nothing reads or that
+    // meet zero probabilities.
     const int ratio = R.Hr / R.Hkv;
     const int kv0 = (8 * grp) / ratio;
     const int nkv = min(8 * grp + 7, R.Hr - 1) / ratio - kv0 + 1;
-    auto issue_v = [&](const UnionInfo* ui, int st, char* dst, bool real) {
+    constexpr int KVS = 8 * C::VRPI / 16;
+    const int vrho = wave * C::VRPI + lane / C::VCPR;
+    const int vkk = vrho & 15;
+    const int kvlw = __builtin_amdgcn_readfirstlane(vrho >> 4);
+    const unsigned vchunk = 16u * (unsigned)((lane % C::VCPR) ^ sv_swz<D>(vkk));
+    const unsigned vrowb = (unsigned)R.Hkv * D * 2;
+    const char* vsb[C::VC];
 #pragma unroll
-      for (int i = 0; i < C::VC; ++i) {
-        const int k = wave + kMapWaves * i;
-        const int rho = k * C::VRPI + lane / C::VCPR, p = lane % C::VCPR;
-        const int kvl = rho >> 4, kk = rho & 15;
-        const int kl = 16 * st + kk;                     // key inside the block
-        const int key = real ? ui->j * B + kl : 0;
-        const bool live = real && kvl < nkv && key < ri.klen;
-        size_t tok;
-        if (paged) {
-          int64_t page = live ? ui->page[kl] : 0;
-          page = page < 0 ? 0 : (page >= R.num_pages ? R.num_pages - 1 : page);
-          tok = live ? (size_t)page * R.page_size + key % R.page_size : 0;
-        } else {
-          tok = (size_t)ri.k0 + (live ? key : 0);
-        }
-        async_copy16(vbase + (tok * R.Hkv + kv0 + (live ? kvl : 0)) * D + 8 * (p ^ sv_swz<D>(kk)),
-                     dst + (size_t)k * 1024);
+    for (int i = 0; i < C::VC; ++i)
+      vsb[i] = vlayer + (size_t)(kv0 + min(kvlw + KVS * i, nkv - 1)) * D * 2;
+    // the rows of step st_ of block j (union slot ui); dummies past the union
+    auto issue_v = [&](const UnionInfo* ui, int jr, int st_, char* dst, bool real) {
+      const int j = real ? jr : 0;
+      unsigned tok;
+      if (!paged) {
+        tok = (unsigned)ri.k0 + (real ? (unsigned)min(j * B + 16 * st_ + vkk, ri.klen - 1) : 0u);
+      } else {
+        // page ids of keys past the sequence repeat its last key's page
+        const int kl = 16 * st_ + vkk;
+        int64_t page = real ? ui->page[kl] : 0;
+        page = page < 0 ? 0 : (page >= R.num_pages ? R.num_pages - 1 : page);
+        const int key = real ? min(j * B + kl, ri.klen - 1) : 0;
+        tok = (unsigned)page * (unsigned)R.page_size + (unsigned)(key % R.page_size);
       }
+      copy_v<C::VC>(tok * vrowb + vchunk, vsb, lds_addr(dst + (size_t)wave * 1024));
     };
 
     // ---- this wave's roles
@@ -475,18 +565,38 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
                                         (q & 7) * 2);
         }
       }
-    // P.V: receiver head 8 grp + wave, its value head in the V buffer
+    // mixed-map writes: lane (lg, r) stores queries mq0 + 16 qi + 4 lg + 0..3
+    // of receiver head r.  Keys 0..3 of a step go to S (two step parities,
+    // 512 bytes apart), keys 4..15 to A (stage p at +512 (p - 1)); lanes of
+    // the padding heads r >= 8 write the dump area.
+    auto chunk_off = [](int q, int swz) { return (((q >> 3) ^ swz) << 4) + (q & 7) * 2; };
+    unsigned wS[2], wA[2][2];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int qq = mq0 + 16 * qi + 4 * lg;
+      const unsigned dump = (unsigned)(C::DOFF + 8 * (8 * lg + (l16 & 7)));
+      wS[qi] = l16 < 8 ? (unsigned)(C::SOFF + l16 * C::SHS + mkey * C::PROW + chunk_off(qq, sa_swz(mkey))) : dump;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        wA[qi][h2] = l16 < 8 ? (unsigned)(C::AOFF + l16 * C::AHS + mkey * C::PROW +
+                                          chunk_off(qq, sa_swz(8 * h2 + mkey)))
+                             : dump;
+    }
+    // P.V: receiver head 8 grp + wave, its value head in the V buffer.  The
+    // A operand of query tile qt: lane L takes queries 32 qt + L % 32 and keys
+    // 8 (L / 32) + 0..7, two transposing reads (keys +0..3 from S or A,
+    // +4..7 from A).
     const int kvl = min((8 * grp + wave) / ratio - kv0, KVC - 1);
-    const char* asrc = abuf + (size_t)wave * C::AHS;
-    unsigned aoff[2][2];   // A operand reads (query tile, key half)
+    unsigned ao0[2], ao1[2];
+    const unsigned aopar = lh == 0 ? 4 * C::PROW : 0;   // S's second parity
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int key = 8 * lh + 4 * hh + (l16 >> 2);
-        const int q = 32 * qt + 16 * (lg & 1) + 4 * (l16 & 3);
-        aoff[qt][hh] = (unsigned)(key * C::PROW + (((q >> 3) ^ sa_swz(key)) << 4) + (q & 7) * 2);
-      }
+    for (int qt = 0; qt < 2; ++qt) {
+      const int q = 32 * qt + 16 * (lg & 1) + 4 * (l16 & 3);
+      const int k0 = 8 * lh + (l16 >> 2), k1 = k0 + 4;
+      ao0[qt] = lh == 0 ? (unsigned)(C::SOFF + wave * C::SHS + k0 * C::PROW + chunk_off(q, sa_swz(k0)))
+                        : (unsigned)(C::AOFF + wave * C::AHS + (k0 - 4) * C::PROW + chunk_off(q, sa_swz(k0)));
+      ao1[qt] = (unsigned)(C::AOFF + wave * C::AHS + (k1 - 4) * C::PROW + chunk_off(q, sa_swz(k1)));
+    }
     unsigned voff[C::NT][2];
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt)
@@ -494,7 +604,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       for (int hh = 0; hh < 2; ++hh) {
         const int key = 8 * lh + 4 * hh + (l16 >> 2);
         const int n = 32 * nt + 16 * (lg & 1) + 4 * (l16 & 3);
-        voff[nt][hh] = (unsigned)((kvl * 16 + key) * C::VROW + (((n >> 3) ^ sv_swz<D>(key)) << 4) + (n & 7) * 2);
+        voff[nt][hh] = (unsigned)(C::VOFF + (kvl * 16 + key) * C::VROW + (((n >> 3) ^ sv_swz<D>(key)) << 4) + (n & 7) * 2);
       }
 
     // W of the current block as the mix's B operand: lane L supplies receiver
@@ -504,119 +614,156 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     bf16x8 Wk[C::NKC];
     auto prep_w = [&](const UnionInfo* ui) {
       const unsigned long long mk = ui->mask;
-      const bool rok = l16 < 8;
-      const float* wrow = Wsh + (rok ? l16 : 0) * 64;
+      const float* wrow = Wsh + (l16 & 7) * 64 + 8 * lg;
 #pragma unroll
-      for (int kc = 0; kc < C::NKC; ++kc)
+      for (int kc = 0; kc < C::NKC; ++kc) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + 32 * kc);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + 32 * kc + 4);
+        const unsigned bits = l16 < 8 ? (unsigned)(mk >> (32 * kc + 8 * lg)) & 0xffu : 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int h = 32 * kc + 8 * lg + e;
-          Wk[kc][e] = (bf16)((rok && h < 64 && ((mk >> h) & 1ull)) ? wrow[h] : 0.f);
-        }
+        for (int e = 0; e < 8; ++e)
+          Wk[kc][e] = (bf16)(((bits >> e) & 1u) ? (e < 4 ? w0[e] : w1[e - 4]) : 0.f);
+      }
     };
 
     prep_p(&UI[0]);
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t) issue_next_p();
+    for (int t = 0; t < NS - 1; ++t) issue_p(t);
 
     bf16x8 Aop[2];
-    int st = 0, crot = 0, mslot = 0;      // step in block, UI slot of its block, ring slot being mixed
+    int st = 0, crot = 0, jcur = 0;       // step in block, its UI slot and column block
+    int mslot = 0, pslot = NS - 1;        // ring slots mixed / filled (rings of other than 4 slots)
     bool mixing = true, pvv = false;      // this step mixes; the previous one did (its P.V runs now)
-    for (int T = 0;; ++T) {
-      // one 16-key step: four stages p = 0..3 with compile-time roles
-      auto stage = [&](auto PP) -> bool {
-        constexpr int p = decltype(PP)::value;
-        // the wave's copies of this stage and everything older have landed
-        wait_vmcnt<C::allow(p)>();
-        __syncthreads();
-        if constexpr (p == 0) {
-          if (mixing && st == 0 && UI[crot].j == kNoColumn) mixing = false;
-          if (!mixing && !pvv) return false;
-          if (pvv) {
-            // the previous step's mixed map as P.V operands: lane L gets
-            // queries 32 qt + L % 32, keys 8 (L / 32) + 0..7
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-              const bf16x4 lo = tr_read(asrc, aoff[qt][0]);
-              const bf16x4 hi = tr_read(asrc, aoff[qt][1]);
-              Aop[qt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-          }
-          // every wave holds its operands before this step's mix overwrites them
-          __syncthreads();
-          if (mixing && st == 0) prep_w(&UI[crot]);
+    // one stage p of a step of parity PAR
+    auto stage = [&](auto PP, auto PAR) -> bool {
+      constexpr int p = decltype(PP)::value;
+      constexpr int par = decltype(PAR)::value;
+      // the wave's copies of this stage and everything older have landed
+      wait_vmcnt<C::allow(p)>();
+      __syncthreads();
+      if constexpr (p == 0) {
+        if (mixing && st == 0) {
+          jcur = __builtin_amdgcn_readfirstlane(UI[crot].j);
+          if (jcur == kNoColumn) mixing = false;
         }
-        // copies: the step's V rows, the union two blocks ahead, P of the
-        // stage NS - 1 ahead
-        if constexpr (p == C::VPART)
-          issue_v(&UI[crot], st, vbuf + (size_t)(NVB == 2 ? (T & 1) : 0) * C::VB, mixing);
-        if constexpr (p == 1)
-          if (mixing && st == 0 && wave == 0) merge(&UI[crot == 0 ? 2 : crot - 1]);
-        issue_next_p();
-
-        // ---- head mix of this stage: key mkey, queries mq0 .. mq0 + 31
-        if (mixing) {
-          const char* slot = ring + (size_t)mslot * C::SLOT;
-          constexpr int kb = 4 * p;                       // first key of the stage inside the step
-          const int akey = kb + mkey;
+        if (!mixing && !pvv) return false;
+      }
+      const int ms = NS == 4 ? p : mslot;
+      const int is = NS == 4 ? (p + 3) & 3 : pslot;
+      // ---- LDS reads first: the mix operands, the previous step's mixed map
+      // (stage 0), the V rows of this stage's P.V
+      bf16x4 mp[2][C::NKC][2];
+      if (mixing) {
 #pragma unroll
-          for (int qi = 0; qi < 2; ++qi) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-            for (int kc = 0; kc < C::NKC; ++kc) {
-              bf16x4 part[2];
+          for (int kc = 0; kc < C::NKC; ++kc)
 #pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                // a transposing read hands each lane values from rows other
-                // lanes of its 16-lane group address, so it never runs under
-                // a partial exec mask: unstaged quads read heads 0..3 and
-                // take a zero operand
-                const bf16x4 v = tr_read(slot, moff[kc][hh][qi]);
-                part[hh] = mstaged[kc][hh] ? v : bf16x4{};
-              }
-              const bf16x8 op = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, Wk[kc], acc, 0, 0, 0);
+            for (int hh = 0; hh < 2; ++hh) {
+              // a transposing read hands each lane values from rows other
+              // lanes of its 16-lane group address, so it never runs under a
+              // partial exec mask: unstaged quads read heads 0..3 and take a
+              // zero operand
+              const bf16x4 v = tr_read(smem, moff[kc][hh][qi] + (unsigned)(ms * C::SLOT));
+              mp[qi][kc][hh] = mstaged[kc][hh] ? v : bf16x4{};
             }
-            // lane (lg, r): queries mq0 + 16 qi + 4 lg + i of receiver head r
-            if (l16 < 8) {
-              const int qq = mq0 + 16 * qi + 4 * lg;
-              bf16x4 o4;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o4[i] = (bf16)acc[i];
-              const unsigned off = (unsigned)(l16 * C::AHS + akey * C::PROW + (((qq >> 3) ^ sa_swz(akey)) << 4) +
-                                              (qq & 7) * 2);
-              *reinterpret_cast<bf16x4*>(abuf + off) = o4;
-            }
-          }
-        }
-        mslot = mslot + 1 == NS ? 0 : mslot + 1;
-
-        // ---- P.V of the previous step: one 32-wide n tile per stage (two
-        // V buffers) or all of d at the first stage (one buffer)
+      }
+      if constexpr (p == 0) {
         if (pvv) {
-          const char* vsrc = vbuf + (size_t)(NVB == 2 ? ((T - 1) & 1) : 0) * C::VB;
 #pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt) {
-            if (NVB == 2 ? nt != p : p != 0) continue;
-            const bf16x4 lo = tr_read(vsrc, voff[nt][0]);
-            const bf16x4 hi = tr_read(vsrc, voff[nt][1]);
-            const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int qt = 0; qt < 2; ++qt) {
+            const bf16x4 lo = tr_read(smem, ao0[qt] + (par == 0 ? aopar : 0u));   // previous step: parity par ^ 1
+            const bf16x4 hi = tr_read(smem, ao1[qt]);
+            Aop[qt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+      }
+      constexpr int vpar = NVB == 2 ? (par ^ 1) : 0;     // V buffer of the previous step
+      constexpr int NTS = NVB == 2 ? 1 : C::NT;           // n tiles of P.V at this stage
+      constexpr int nt0 = NVB == 2 ? p : 0;
+      constexpr bool pv_here = NVB == 2 ? p < C::NT : p == 0;
+      bf16x8 vop[NTS];
+      if constexpr (pv_here) {
+        if (pvv) {
+#pragma unroll
+          for (int t = 0; t < NTS; ++t) {
+            const bf16x4 lo = tr_read(smem, voff[nt0 + t][0] + vpar * C::VB);
+            const bf16x4 hi = tr_read(smem, voff[nt0 + t][1] + vpar * C::VB);
+            vop[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+      }
+      if constexpr (p == 0)
+        if (mixing && st == 0) prep_w(&UI[crot]);
+
+      // ---- copies: the step's V rows, the union two blocks ahead, P of the
+      // stage NS - 1 ahead
+      if constexpr (p == C::VPART)
+        issue_v(&UI[crot], jcur, st, vbuf + (size_t)(NVB == 2 ? par : 0) * C::VB, mixing);
+      if constexpr (p == 1) {
+        if (mixing && st == 0 && wave == 0) merge(&UI[crot == 0 ? 2 : crot - 1]);
+        else merge_dummy();
+      }
+      issue_p(is);
+      if constexpr (NS != 4) {
+        mslot = mslot + 1 == NS ? 0 : mslot + 1;
+        pslot = pslot + 1 == NS ? 0 : pslot + 1;
+      }
+
+      // ---- head mix of this stage (key 4 p + mkey, queries mq0 .. mq0 + 31),
+      // then P.V of the previous step on the matrix pipe while the mix's
+      // results are converted and stored
+      f32x4 acc[2];
+      if (mixing) {
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          acc[qi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < C::NKC; ++kc) {
+            const bf16x8 op = __builtin_shufflevector(mp[qi][kc][0], mp[qi][kc][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[qi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, Wk[kc], acc[qi], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (pv_here) {
+        if (pvv) {
+#pragma unroll
+          for (int t = 0; t < NTS; ++t)
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
-              O[qt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aop[qt], vop, O[qt][nt], 0, 0, 0);
-          }
+              O[qt][nt0 + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aop[qt], vop[t], O[qt][nt0 + t], 0, 0, 0);
         }
-        return true;
-      };
-      if (!stage(IC<0>{})) break;
-      stage(IC<1>{});
-      stage(IC<2>{});
-      stage(IC<3>{});
+      }
+      if (mixing) {
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          bf16x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = (bf16)acc[qi][i];
+          const unsigned off = p == 0 ? wS[qi] + par * 4 * C::PROW : wA[qi][p >> 1] + (p - 1) * 4 * C::PROW;
+          *reinterpret_cast<bf16x4*>(smem + off) = o4;
+        }
+      }
+      return true;
+    };
+    auto end_step = [&]() {
       pvv = mixing;
       if (mixing && ++st == C::SB) {
         st = 0;
         crot = crot == kUnionSlots - 1 ? 0 : crot + 1;
       }
+    };
+    for (;;) {
+      if (!stage(IC<0>{}, IC<0>{})) break;
+      stage(IC<1>{}, IC<0>{});
+      stage(IC<2>{}, IC<0>{});
+      stage(IC<3>{}, IC<0>{});
+      end_step();
+      if (!stage(IC<0>{}, IC<1>{})) break;
+      stage(IC<1>{}, IC<1>{});
+      stage(IC<2>{}, IC<1>{});
+      stage(IC<3>{}, IC<1>{});
+      end_step();
     }
   }
 
@@ -745,6 +892,9 @@ int launch_gd(const MappedArgs& a, void* stream) {
 static bool mapped_mfma_plan(const MappedArgs& a, mf_dtype dt, bool allow_fast, size_t lds_limit, int* kvc, int* ns,
                              int* nvb) {
   if (dt != MF_BF16 || !allow_fast || (a.B != 64 && a.B != 128) || (a.d != 64 && a.d != 128)) return false;
+  // V rows are addressed by 32-bit byte offsets inside one layer
+  for (int k = 0; k < a.nrecv; ++k)
+    if ((uint64_t)a.rx[k].vrows * (uint64_t)a.rx[k].Hkv * (uint64_t)a.d * 2u > 0xFFFFFFFFull) return false;
   *kvc = max_group_value_heads(a) <= 4 ? 4 : 8;
   const int hp = (a.Hs + 15) / 16 * 16;
   return map_plan(a.B, a.d, hp, *kvc, lds_limit, ns, nvb);
