@@ -28,6 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HEADLINE = ("bf16 causal 8192 tokens, 16 mapped layers, sender 32 heads -> receiver 24 heads, d=128, B=64, "
+            "structured Q/K")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_bf16_8k_16layers.json")
 KERNEL_SOURCES = {
@@ -62,6 +64,12 @@ def parse():
                     help="only time the 8K step over layer groups, the fused step of a group overlapping "
                          "the next group's statistics on a second stream")
     ap.add_argument("--groups", type=int, default=4, help="layer groups of --pipelined")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the headline sweep: the 8K 16-layer step at tau 0.90 / 0.95 / 0.99 and the "
+                         "4K single-layer step, one line each with the per-kernel targets")
+    ap.add_argument("--long-context", action="store_true",
+                    help="only the 32K one-sender / two-receiver workload: statistics, compression and both "
+                         "receivers' fused steps, each with its roofline")
     return ap.parse_args()
 
 
@@ -318,6 +326,7 @@ def varlen_bench(reps: int):
     L = wl.num_layers
     steps = []
     tot_q = 0
+    map_bytes = 0
     for step in range(synth.num_chunk_steps(wl)):
         lay = synth.batch_layout(wl, step)
         ins = [synth.layer_inputs(wl, l, step, lay) for l in range(L)]
@@ -335,6 +344,11 @@ def varlen_bench(reps: int):
         desc = mf.receiver_desc(pool, wl.H_s, wl.H_r, wl.d, wl.B, list(range(L)), L, out[0].numel(),
                                 st.col_idx.numel(), bt, wl.page_size)
         steps.append((batch, q, k, st, cap, desc, W, pool, out))
+        # fused step's algorithmic bytes: kept values, row_ptr, col_idx, the
+        # V rows of every key once, W, O once
+        nrows = L * wl.H_s * batch.total_rowblocks
+        map_bytes += (cap * wl.B * wl.B * 2 + (nrows + 1) * 4 + cap * 4 + L * lay.total_k * wl.hkv_r * wl.d * 2
+                      + L * wl.H_r * wl.H_s * 4 + L * lay.total_q * wl.H_r * wl.d * 2)
         tot_q += lay.total_q
         print(f"[bench] chunk step {step}: {lay.total_q} query rows, {cap} kept blocks", file=sys.stderr, flush=True)
 
@@ -349,13 +363,21 @@ def varlen_bench(reps: int):
         for b in steps:
             one(b)
 
+    def all_mapped():
+        for batch, q, k, st, cap, desc, W, pool, out in steps:
+            mf.mapped_attn_v(desc, batch, st.row_ptr, st.col_idx, st.values, W, pool, out)
+
     ms = _event_ms(all_steps, reps)
+    ms_map = _event_ms(all_mapped, reps)
+    map_gbs = map_bytes / (ms_map * 1e-3) / 1e9
     _emit({"metric": "whole path over every prefill chunk step, varlen / chunked / paged",
                       "config": {"workload": "bf16, 32 sequences lognormal(7.5, 0.8) lengths in [256, 16384], "
                                              "chunks of 2048 query rows, 16-token pages, 32 -> 24 heads, d=128, B=64",
                                  "layers_timed": L, "tau": wl.tau, "chunk_steps": len(steps),
                                  "query_rows": tot_q, "kept_blocks": int(sum(b[4] for b in steps))},
-                      "ms_all_steps": round(ms, 3), "tokens_per_s": round(tot_q / (ms * 1e-3), 1)})
+                      "ms_all_steps": round(ms, 3), "tokens_per_s": round(tot_q / (ms * 1e-3), 1),
+                      "mapped_attn_v": {"ms_all_steps": round(ms_map, 3), "algorithmic_bytes": int(map_bytes),
+                                        "GB_per_s": round(map_gbs, 1), "hbm_frac": round(map_gbs / HBM_PEAK_GBS, 4)}})
 
 
 def several_receivers_bench(reps: int):
@@ -450,6 +472,256 @@ def pipelined_bench(reps: int, tau: float, layers: int, groups: int):
                       "results": res})
 
 
+def measure_path(wl, tau: float, steps: int, warmup: int, workload_name: str):
+    """Time `steps` whole-path steps (statistics, compression, fused step,
+    each bracketed by HIP events on the launch stream) of workload `wl` at
+    threshold tau, inputs resident in HBM.  Returns the bench record and the
+    sender state."""
+    import torch
+
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    L = wl.num_layers
+    print(f"[bench] generating {L} layers of {wl.name}", file=sys.stderr, flush=True)
+    lay = synth.batch_layout(wl)
+    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(L)]
+    q = torch.stack([x.q for x in ins]).to(dev)
+    k = torch.stack([x.k for x in ins]).to(dev)
+    v = torch.stack([x.v for x in ins]).to(dev)
+    W = torch.stack([x.w for x in ins]).to(dev)
+    del ins
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    cap = pipeline.count_capacity(batch, q, k, wl.B, tau)
+    st = pipeline.alloc_sender(batch, q, k, wl.B, cap)
+    out = torch.empty((L, lay.total_q, wl.H_r, wl.d), dtype=torch.bfloat16, device=dev)
+    lmap = list(range(L))
+    desc_r = mf.receiver_desc(v, wl.H_s, wl.H_r, wl.d, wl.B, lmap, L, out[0].numel(), st.col_idx.numel())
+    stream = torch.cuda.current_stream()
+    print(f"[bench] nnz={cap} blocks ({cap * wl.B * wl.B * 2 / 1e9:.2f} GB of values)", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass, st.stats_workspace)
+        if ev is not None:
+            ev[1].record(stream)
+        mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, tau, st.row_ptr,
+                           st.col_idx, st.values, cap, st.workspace, sync_count=False)
+        if ev is not None:
+            ev[2].record(stream)
+        mf.mapped_attn_v(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    d_stats = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    d_comp = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    d_map = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    d_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    t_stats, t_comp, t_map = d_stats.mean() * 1e-3, d_comp.mean() * 1e-3, d_map.mean() * 1e-3
+
+    def spread(d):
+        return {"median": round(float(np.median(d)), 4), "p10": round(float(np.percentile(d, 10)), 4),
+                "p90": round(float(np.percentile(d, 90)), 4)}
+    ms_per_step = wall / steps * 1e3
+    assert int(st.row_ptr[-1]) == cap
+
+    N = lay.total_q
+    # algorithmic work (see the design notes): one causal Q K^T for the stats;
+    # kept values + row_ptr + col_idx + V once + W + O once for the fused kernel
+    stats_flops = L * wl.H_s * N * (N + 1) / 2 * 2 * wl.d
+    nrows = L * wl.H_s * batch.total_rowblocks
+    map_bytes = (cap * wl.B * wl.B * 2 + (nrows + 1) * 4 + cap * 4 + L * N * wl.hkv_r * wl.d * 2
+                 + L * wl.H_r * wl.H_s * 4 + L * N * wl.H_r * wl.d * 2)
+    stats_tflops = stats_flops / t_stats / 1e12
+    map_gbs = map_bytes / t_map / 1e9
+    rooflines = {
+        "stats_mfma_kernel": {"bound": "mfma", "achieved": round(stats_tflops, 2),
+                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(stats_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "traffic": measured_traffic("stats_mfma_kernel"),
+                               "us_per_launch": round(t_stats * 1e6, 1)},
+        "mapped_mfma_kernel": {"bound": "hbm", "achieved": round(map_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(map_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic("mapped_mfma_kernel"),
+                   "us_per_launch": round(t_map * 1e6, 1)},
+    }
+    dominant = max(("stats_mfma_kernel", t_stats), ("mapped_mfma_kernel", t_map), key=lambda x: x[1])[0]
+    res = {
+        "metric": "mapped-attn·V GB/s & % HBM peak; block-compress tokens/s at 8K ctx",
+        "value": round(N / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_name,
+                   "seq_len": N, "layers": L, "tau": tau, "B": wl.B, "H_s": wl.H_s,
+                   "H_r": wl.H_r, "d": wl.d},
+        "mapped_attn_v": {"GB_per_s": round(map_gbs, 1), "hbm_frac": round(map_gbs / HBM_PEAK_GBS, 4),
+                          "us_per_layer": round(t_map / L * 1e6, 1),
+                          "tokens_per_s": round(N * L / t_map, 1)},
+        "block_compress": {"tokens_per_s": round(N / (t_stats + t_comp), 1),
+                           "us_per_layer": round((t_stats + t_comp) / L * 1e6, 1),
+                           "stats_us_per_layer": round(t_stats / L * 1e6, 1),
+                           "select_extract_us_per_layer": round(t_comp / L * 1e6, 1)},
+        # per-launch durations in ms (HIP events on the launch stream); the
+        # 8K step's working set (about 15 GB) is far beyond the 256 MB
+        # Infinity Cache, so consecutive steps do not run warm
+        "timing_ms": {"step": spread(d_step), "block_stats": spread(d_stats),
+                      "select_scan_extract": spread(d_comp), "mapped_attn_v": spread(d_map)},
+        "kept_blocks": cap,
+        "kept_fraction": round(cap / (L * wl.H_s * sum(i + 1 for i in range(batch.total_rowblocks))), 4),
+        "roofline": {k_: v_ for k_, v_ in rooflines[dominant].items() if k_ != "us_per_launch"},
+        "roofline_kernel": dominant,
+        "rooflines": rooflines,
+    }
+    return res, st, batch, cap, lay
+
+
+def union_stats(st, batch, cap, wl) -> dict:
+    """Union of the sender heads' kept sets per (layer, row-block): its size
+    against the causal blocks, and how many heads keep each union block."""
+    rp_h = st.row_ptr.cpu().numpy().astype(np.int64)
+    rows = np.repeat(np.arange(len(rp_h) - 1), np.diff(rp_h))
+    R = batch.total_rowblocks
+    ukeys = ((rows // (wl.H_s * R)) * R + rows % R) * batch.max_colblocks + \
+        st.col_idx[:cap].cpu().numpy().astype(np.int64)
+    union = int(np.unique(ukeys).size)
+    return {"union_blocks": union,
+            "union_density": round(union / (wl.num_layers * sum(i + 1 for i in range(R))), 4),
+            "head_overlap": round(cap / (wl.H_s * union), 4)}
+
+
+# fused-step time per layer that 60% of the HBM peak implies, by workload and
+# tau (the algorithmic bytes at the generator's kept fractions / 4.8 TB/s)
+K3_TARGET_US = {("8k", 0.90): 57.0, ("8k", 0.95): 84.0, ("8k", 0.99): 188.0, ("4k", 0.95): 28.0}
+STATS_TARGET_FRAC = 0.40
+
+
+def sweep_bench(steps: int, warmup: int):
+    """The headline sweep: 8K x 16 layers at tau 0.90 / 0.95 / 0.99, and the
+    4K single-layer step; one record each, with the per-kernel targets."""
+    import torch
+
+    from cross_model_attention_mf_amd import synth
+    cases = [("8k", synth.workload_by_id(3), t, HEADLINE) for t in (0.90, 0.95, 0.99)]
+    cases.append(("4k", synth.workload_by_id(2), 0.95,
+                  "bf16 causal 4096 tokens, one mapped layer, sender 32 heads -> receiver 24 heads, d=128, B=64, "
+                  "structured Q/K"))
+    for tag, wl, tau, name in cases:
+        res, st, batch, cap, _ = measure_path(wl, tau, steps, warmup, name)
+        res.update(union_stats(st, batch, cap, wl))
+        tgt = K3_TARGET_US[(tag, tau)]
+        res["metric"] = f"headline sweep: {tag} step at tau {tau}"
+        res["targets"] = {"mapped_attn_v_us_per_layer": tgt,
+                          "mapped_attn_v_meets": bool(res["mapped_attn_v"]["us_per_layer"] <= tgt),
+                          "block_stats_frac": STATS_TARGET_FRAC,
+                          "block_stats_meets": bool(res["rooflines"]["stats_mfma_kernel"]["frac"] >= STATS_TARGET_FRAC)}
+        _emit(res)
+        del st
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def long_context_bench(steps: int, warmup: int):
+    """32K, B=128: one 40-head sender's statistics and compression, then the
+    fused step of receivers of 32 and 24 heads, one launch each on two
+    streams and one launch for both; every kernel with its roofline."""
+    import torch
+
+    from cross_model_attention_mf_amd import mapflow as mf
+    from cross_model_attention_mf_amd import pipeline, synth
+    dev = torch.device("cuda")
+    wl = synth.workload_by_id(5)
+    lay = synth.batch_layout(wl)
+    x = synth.layer_inputs(wl, 0, layout=lay)
+    q, k = x.q[None].to(dev), x.k[None].to(dev)
+    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
+    cap = pipeline.count_capacity(batch, q, k, wl.B, wl.tau)
+    st = pipeline.alloc_sender(batch, q, k, wl.B, cap)
+    recv = [(x.w[None].to(dev), x.v[None].to(dev))]
+    recv += [(w[None].to(dev), v[None].to(dev)) for w, v in zip(x.extra_w, x.extra_v)]
+    del x
+
+    def stats():
+        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass, st.stats_workspace)
+
+    def compress():
+        mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, wl.tau, st.row_ptr, st.col_idx,
+                           st.values, cap, st.workspace, sync_count=False)
+
+    for _ in range(warmup):
+        stats(); compress()
+    torch.cuda.synchronize()
+    st.nnz = cap
+    t_stats, t_comp = _event_ms(stats, steps), _event_ms(compress, steps)
+    ss = [torch.cuda.Stream() for _ in recv]
+
+    def two_streams():
+        cur, outs = torch.cuda.current_stream(), []
+        for s in ss:
+            s.wait_stream(cur)
+        for (W, v), s in zip(recv, ss):
+            with torch.cuda.stream(s):
+                outs.append(pipeline.mapped(st, W, v, [0], stream=s))
+        for s in ss:
+            cur.wait_stream(s)
+        return outs
+
+    def one_launch():
+        return pipeline.mapped_multi(st, recv, [0])
+
+    def each(i):
+        W, v = recv[i]
+        return lambda: pipeline.mapped(st, W, v, [0])
+
+    for _ in range(warmup):
+        two_streams(); one_launch()
+    torch.cuda.synchronize()
+    t_each = [_event_ms(each(i), steps) for i in range(len(recv))]
+    t_two, t_one = _event_ms(two_streams, steps), _event_ms(one_launch, steps)
+    N = lay.total_q
+    flops = wl.H_s * N * (N + 1) / 2 * 2 * wl.d
+    nrows = wl.H_s * batch.total_rowblocks
+    shared = cap * wl.B * wl.B * 2 + (nrows + 1) * 4 + cap * 4
+    rec = []
+    for i, (W, v) in enumerate(recv):
+        hr, hkv = W.shape[1], v.shape[2]
+        byts = shared + N * hkv * wl.d * 2 + hr * wl.H_s * 4 + N * hr * wl.d * 2
+        gbs = byts / (t_each[i] * 1e-3) / 1e9
+        rec.append({"H_r": hr, "H_kv": hkv, "algorithmic_bytes": byts, "ms": round(t_each[i], 3),
+                    "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    tf = flops / (t_stats * 1e-3) / 1e12
+    _emit({"metric": "32K one sender, two receivers: every stage with its roofline",
+           "config": {"workload": "bf16 causal 32768 tokens, sender 40 heads, d=128, B=128, receivers 32 and 24 "
+                                  "heads", "tau": wl.tau, "kept_blocks": cap,
+                      "kept_value_bytes": cap * wl.B * wl.B * 2},
+           "block_stats": {"ms": round(t_stats, 3), "TFLOP_per_s": round(tf, 1),
+                           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+           "select_scan_extract": {"ms": round(t_comp, 3),
+                                   "write_GB_per_s": round(cap * wl.B * wl.B * 2 / (t_comp * 1e-3) / 1e9, 1)},
+           "block_compress_tokens_per_s": round(N / ((t_stats + t_comp) * 1e-3), 1),
+           "mapped_attn_v": {"per_receiver_one_stream": rec, "two_streams_ms": round(t_two, 3),
+                             "one_launch_for_both_ms": round(t_one, 3),
+                             "target_ms_each": [2.51, 2.48]}})
+
+
 def source_hash(rel: str) -> str:
     with open(os.path.join(ROOT, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -511,7 +783,10 @@ def cpu_baseline(wl, tau, n_layers):
     per_step = wl.num_layers / n_layers
     threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
     rate = lambda t: round(lay.total_q / (t * per_step), 3)
+    # the oracle's loops are single-threaded Python around numpy; its matrix
+    # products use the BLAS pool
     return {"value": rate(dt), "unit": "tokens/s", "cores": int(threads),
+            "cores_available": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
             "kind": "oracle",
             "stages_tokens_per_s": {"block_stats": rate(t_stats), "select_extract": rate(t_sel),
                                     "mapped_attn_v": rate(t_map)},
@@ -553,6 +828,12 @@ def main():
     if args.pipelined:
         pipelined_bench(max(args.steps, 3), args.tau, args.layers, args.groups)
         return
+    if args.sweep:
+        sweep_bench(max(args.steps, 3), args.warmup)
+        return
+    if args.long_context:
+        long_context_bench(max(args.steps, 3), args.warmup)
+        return
 
     if args.copy_calibration:
         n = 1 << 30
@@ -567,115 +848,7 @@ def main():
     wl = synth.workload_by_id(3).replace(num_layers=args.layers)
     tau = args.tau
     L = wl.num_layers
-    print(f"[bench] generating {L} layers of {wl.name}", file=sys.stderr, flush=True)
-    lay = synth.batch_layout(wl)
-    ins = [synth.layer_inputs(wl, l, layout=lay) for l in range(L)]
-    q = torch.stack([x.q for x in ins]).to(dev)
-    k = torch.stack([x.k for x in ins]).to(dev)
-    v = torch.stack([x.v for x in ins]).to(dev)
-    W = torch.stack([x.w for x in ins]).to(dev)
-    del ins
-    batch = mf.Batch(lay.cu_seqlens_q, lay.cu_seqlens_k, None, wl.B)
-    cap = pipeline.count_capacity(batch, q, k, wl.B, tau)
-    st = pipeline.alloc_sender(batch, q, k, wl.B, cap)
-    out = torch.empty((L, lay.total_q, wl.H_r, wl.d), dtype=torch.bfloat16, device=dev)
-    lmap = list(range(L))
-    desc_r = mf.receiver_desc(v, wl.H_s, wl.H_r, wl.d, wl.B, lmap, L, out[0].numel(), st.col_idx.numel())
-    stream = torch.cuda.current_stream()
-    print(f"[bench] nnz={cap} blocks ({cap * wl.B * wl.B * 2 / 1e9:.2f} GB of values)", file=sys.stderr, flush=True)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        mf.block_stats(st.desc, batch, q, k, st.row_lse, st.block_mass, st.stats_workspace)
-        if ev is not None:
-            ev[1].record(stream)
-        mf.compress_blocks(st.desc, batch, q, k, st.row_lse, st.block_mass, tau, st.row_ptr,
-                           st.col_idx, st.values, cap, st.workspace, sync_count=False)
-        if ev is not None:
-            ev[2].record(stream)
-        mf.mapped_attn_v(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    d_stats = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    d_comp = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    d_map = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    d_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    t_stats, t_comp, t_map = d_stats.mean() * 1e-3, d_comp.mean() * 1e-3, d_map.mean() * 1e-3
-
-    def spread(d):
-        return {"median": round(float(np.median(d)), 4), "p10": round(float(np.percentile(d, 10)), 4),
-                "p90": round(float(np.percentile(d, 90)), 4)}
-    ms_per_step = wall / args.steps * 1e3
-    assert int(st.row_ptr[-1]) == cap
-
-    N = lay.total_q
-    # algorithmic work (see the design notes): one causal Q K^T for the stats;
-    # kept values + row_ptr + col_idx + V once + W + O once for the fused kernel
-    stats_flops = L * wl.H_s * N * (N + 1) / 2 * 2 * wl.d
-    nrows = L * wl.H_s * batch.total_rowblocks
-    map_bytes = (cap * wl.B * wl.B * 2 + (nrows + 1) * 4 + cap * 4 + L * N * wl.hkv_r * wl.d * 2
-                 + L * wl.H_r * wl.H_s * 4 + L * N * wl.H_r * wl.d * 2)
-    stats_tflops = stats_flops / t_stats / 1e12
-    map_gbs = map_bytes / t_map / 1e9
-    rooflines = {
-        "stats_mfma_kernel": {"bound": "mfma", "achieved": round(stats_tflops, 2),
-                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": round(stats_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                               "traffic": measured_traffic("stats_mfma_kernel"),
-                               "us_per_launch": round(t_stats * 1e6, 1)},
-        "mapped_mfma_kernel": {"bound": "hbm", "achieved": round(map_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(map_gbs / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic("mapped_mfma_kernel"),
-                   "us_per_launch": round(t_map * 1e6, 1)},
-    }
-    dominant = max(("stats_mfma_kernel", t_stats), ("mapped_mfma_kernel", t_map), key=lambda x: x[1])[0]
-    res = {
-        "metric": "mapped-attn·V GB/s & % HBM peak; block-compress tokens/s at 8K ctx",
-        "value": round(N / (ms_per_step * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "bf16 causal 8192 tokens, 16 mapped layers, sender 32 heads -> "
-                               "receiver 24 heads, d=128, B=64, structured Q/K",
-                   "seq_len": N, "layers": L, "tau": tau, "B": wl.B, "H_s": wl.H_s,
-                   "H_r": wl.H_r, "d": wl.d},
-        "mapped_attn_v": {"GB_per_s": round(map_gbs, 1), "hbm_frac": round(map_gbs / HBM_PEAK_GBS, 4),
-                          "us_per_layer": round(t_map / L * 1e6, 1),
-                          "tokens_per_s": round(N * L / t_map, 1)},
-        "block_compress": {"tokens_per_s": round(N / (t_stats + t_comp), 1),
-                           "us_per_layer": round((t_stats + t_comp) / L * 1e6, 1),
-                           "stats_us_per_layer": round(t_stats / L * 1e6, 1),
-                           "select_extract_us_per_layer": round(t_comp / L * 1e6, 1)},
-        # per-launch durations in ms (HIP events on the launch stream); one
-        # step's working set (about 15 GB) is far beyond the 256 MB Infinity
-        # Cache, so consecutive steps do not run warm
-        "timing_ms": {"step": spread(d_step), "block_stats": spread(d_stats),
-                      "select_scan_extract": spread(d_comp), "mapped_attn_v": spread(d_map)},
-        "kept_blocks": cap,
-        "kept_fraction": round(cap / (L * wl.H_s * sum(i + 1 for i in range(batch.total_rowblocks))), 4),
-        "roofline": {k_: v_ for k_, v_ in rooflines[dominant].items() if k_ != "us_per_launch"},
-        "roofline_kernel": dominant,
-        "rooflines": rooflines,
-    }
+    res, st, batch, cap, lay = measure_path(wl, tau, args.steps, args.warmup, HEADLINE)
     # a plain 1 GiB device copy as the practical HBM ceiling (read + write
     # bytes over the copy's time), beside the 8 TB/s published peak
     src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -692,18 +865,8 @@ def main():
     copy_gbs = 2 * (1 << 30) * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del src_c, dst_c
     res["hbm_copy_GB_per_s"] = round(copy_gbs, 1)
-    res["mapped_attn_v"]["copy_frac"] = round(map_gbs / copy_gbs, 4)
-    # union of the sender heads' kept sets per (layer, row-block): its size
-    # against the causal blocks, and how many heads keep each union block
-    rp_h = st.row_ptr.cpu().numpy().astype(np.int64)
-    rows = np.repeat(np.arange(len(rp_h) - 1), np.diff(rp_h))
-    R = batch.total_rowblocks
-    ukeys = ((rows // (wl.H_s * R)) * R + rows % R) * batch.max_colblocks + \
-        st.col_idx[:cap].cpu().numpy().astype(np.int64)
-    union = int(np.unique(ukeys).size)
-    res["union_blocks"] = union
-    res["union_density"] = round(union / (L * sum(i + 1 for i in range(R))), 4)
-    res["head_overlap"] = round(cap / (wl.H_s * union), 4)
+    res["mapped_attn_v"]["copy_frac"] = round(res["mapped_attn_v"]["GB_per_s"] / copy_gbs, 4)
+    res.update(union_stats(st, batch, cap, wl))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, tau, min(args.cpu_sample_layers, L))
