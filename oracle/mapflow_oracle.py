@@ -251,7 +251,9 @@ class UnitResult:
 
 
 def compress_unit(q: np.ndarray, k: np.ndarray, rb: RowBlock, h: int, B: int,
-                  tau: float, scale: float, keep_strip: bool = False) -> UnitResult:
+                  tau: float, scale: float, keep_strip: bool = False, extract: bool = True) -> UnitResult:
+    """Steps 1-4 for one unit; extract=False stops after the selection (step
+    3) and leaves values empty."""
     H, H_kv = q.shape[1], k.shape[1]
     qr = q[rb.q0: rb.q0 + rb.rows, h, :]
     kk = k[rb.k0: rb.k0 + rb.klen, kv_head(h, H, H_kv), :]
@@ -261,7 +263,8 @@ def compress_unit(q: np.ndarray, k: np.ndarray, rb: RowBlock, h: int, B: int,
     P, lse = causal_probs(qr, keys, pos, scale)
     m = block_masses(P, B, ncand)
     sel = select_blocks(m, tau)
-    return UnitResult(lse, sel, extract_blocks(P, sel.kept, B), P if keep_strip else None)
+    vals = extract_blocks(P, sel.kept, B) if extract else np.zeros((0, B, B))
+    return UnitResult(lse, sel, vals, P if keep_strip else None)
 
 
 @dataclasses.dataclass
@@ -277,9 +280,10 @@ def compress_layer(q: np.ndarray, k: np.ndarray, cu_q, cu_k, q_pos0, B: int,
                    tau: float, scale: Optional[float] = None,
                    heads: Optional[Iterable[int]] = None,
                    rowblocks: Optional[Iterable[int]] = None,
-                   keep_strips: bool = False) -> LayerCompression:
+                   keep_strips: bool = False, extract: bool = True) -> LayerCompression:
     """q [Tq, H_s, d], k [Tk, H_kv, d] float64 packed; returns steps 1-4 for the
-    requested heads and row-blocks (default: all)."""
+    requested heads and row-blocks (default: all); extract=False stops each
+    unit after its selection."""
     scale = default_scale(q.shape[2]) if scale is None else scale
     rbs = enumerate_rowblocks(cu_q, cu_k, q_pos0, B)
     hs = range(q.shape[1]) if heads is None else heads
@@ -287,7 +291,7 @@ def compress_layer(q: np.ndarray, k: np.ndarray, cu_q, cu_k, q_pos0, B: int,
     units = {}
     for i in which:
         for h in hs:
-            units[(h, i)] = compress_unit(q, k, rbs[i], h, B, tau, scale, keep_strips)
+            units[(h, i)] = compress_unit(q, k, rbs[i], h, B, tau, scale, keep_strips, extract)
     return LayerCompression(rbs, units)
 
 

@@ -11,7 +11,9 @@ Tolerances (written here once, used by every parity test):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 import sys
 import time
 from typing import Dict, List, Optional, Sequence
@@ -126,11 +128,36 @@ def sample_rowblocks(n: int, k: int, seed: int = 0) -> List[int]:
     return sorted({0, n - 1, *[int(x) for x in mid]})
 
 
+def oracle_layer(q64, k64, cu_q, cu_k, p0, B: int, tau: float, heads=None, rowblocks=None,
+                 workers: int = 1, extract: bool = True) -> orc.LayerCompression:
+    """orc.compress_layer, one call per sender head on a thread pool when
+    workers > 1 (numpy releases the GIL in its products and exponentials);
+    the units are merged unchanged."""
+    hs = list(range(q64.shape[1])) if heads is None else list(heads)
+    if workers <= 1 or len(hs) == 1:
+        return orc.compress_layer(q64, k64, cu_q, cu_k, p0, B, tau, heads=hs, rowblocks=rowblocks,
+                                  extract=extract)
+    with concurrent.futures.ThreadPoolExecutor(min(workers, len(hs))) as ex:
+        parts = list(ex.map(lambda h: orc.compress_layer(q64, k64, cu_q, cu_k, p0, B, tau, heads=[h],
+                                                         rowblocks=rowblocks, extract=extract), hs))
+    units = {}
+    for part in parts:
+        units.update(part.units)
+    return orc.LayerCompression(parts[0].rowblocks, units)
+
+
+def host_workers() -> int:
+    """CPU threads for the oracle: the cores this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def check_layer(run: GpuRun, li: int, rowblocks: Optional[Sequence[int]] = None,
                 heads: Optional[Sequence[int]] = None, check_output: bool = True,
-                rep: Optional[Report] = None) -> Report:
+                rep: Optional[Report] = None, check_values: bool = True, workers: int = 1) -> Report:
     """Compare layer index li of a GPU run with the oracle on the given
-    row-blocks (all by default) and sender heads (all by default)."""
+    row-blocks (all by default) and sender heads (all by default): block
+    masses, row LSE and index sets always; stored values when check_values;
+    the receivers' output when check_output (all heads only)."""
     wl, tau, lay = run.wl, run.tau, run.layout
     rep = rep or Report()
     B = wl.B
@@ -139,8 +166,8 @@ def check_layer(run: GpuRun, li: int, rowblocks: Optional[Sequence[int]] = None,
     chunked = wl.chunk is not None
     p0 = lay.q_pos0 if chunked else None
     t0 = time.time()
-    lc = orc.compress_layer(q64, k64, lay.cu_seqlens_q, lay.cu_seqlens_k, p0, B, tau,
-                            heads=heads, rowblocks=rowblocks)
+    lc = oracle_layer(q64, k64, lay.cu_seqlens_q, lay.cu_seqlens_k, p0, B, tau, heads=heads,
+                      rowblocks=rowblocks, workers=workers, extract=check_values or check_output)
     st = run.state
     H = wl.H_s
     nrb = st.batch.total_rowblocks
@@ -176,6 +203,8 @@ def check_layer(run: GpuRun, li: int, rowblocks: Optional[Sequence[int]] = None,
                 override[(h, i)] = cols
                 u = orc.compress_unit(q64, k64, rb, h, B, tau, orc.default_scale(wl.d), keep_strip=True)
                 lc.units[(h, i)] = u
+            if not check_values:
+                continue
             # stored key-major: [e][key][query]
             vals_g = st.values[e0:e1].to(torch.float64).cpu().numpy().transpose(0, 2, 1)
             for t, j in enumerate(cols):

@@ -82,12 +82,18 @@ def test_bf16_4k_workload_sampled():
     parity.log(f"[parity] kept fraction on sampled row-blocks {frac:.3f}")
 
 
-@pytest.mark.parametrize("tau", [0.95, 0.90, 0.99])
-def test_bf16_8k_16_layers_sampled(tau):
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("tau,full_layer", [(0.95, 8), (0.90, 3), (0.99, 12)])
+def test_bf16_8k_16_layers(tau, full_layer):
+    """All 16 layers in one launch per stage (the bench's configuration);
+    sampled row-blocks of the first and last layer, and one whole layer (all
+    128 row-blocks x 32 sender heads: masses, LSE, index sets, values, O)."""
     run = parity.run_gpu(W3, tau, list(range(W3.num_layers)))
     n = run.state.batch.total_rowblocks
     for li in (0, 15):
         parity.check_layer(run, li, rowblocks=parity.sample_rowblocks(n, 3, seed=li))
+    rep = parity.check_layer(run, full_layer, workers=parity.host_workers())
+    assert rep.units == n * W3.H_s
 
 
 def test_varlen_chunked_paged_16_layers_sampled():
@@ -98,10 +104,14 @@ def test_varlen_chunked_paged_16_layers_sampled():
         parity.check_layer(run, 3, rowblocks=parity.sample_rowblocks(n, 4, seed=step))
 
 
+@pytest.mark.timeout(900)
 def test_32k_one_sender_two_receivers_two_streams():
     run = parity.run_gpu(W5, W5.tau, [0], streams=True)
     n = run.state.batch.total_rowblocks
     parity.check_layer(run, 0, rowblocks=[0, n // 2, n - 1])
+    # every row-block and sender head: masses, LSE and index sets
+    rep = parity.check_layer(run, 0, check_output=False, check_values=False, workers=parity.host_workers())
+    assert rep.units == n * W5.H_s
     # the two concurrent launches equal the same launches run one after another
     seq = parity.run_gpu(W5.replace(seqlens=(4096,)), W5.tau, [0], streams=False)
     par = parity.run_gpu(W5.replace(seqlens=(4096,)), W5.tau, [0], streams=True)
