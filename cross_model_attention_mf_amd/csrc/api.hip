@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -188,12 +189,14 @@ size_t mf_compress_workspace_size(const mf_sender_desc* desc, const mf_batch* ba
   return workspace_layout(desc, batch).bytes;
 }
 
-mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
-                             const float* row_lse, const float* block_mass, float tau, int32_t* row_ptr,
-                             int32_t* col_idx, void* values, int64_t capacity_blocks, int64_t* nnz_out,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-  mf::clear_error();
-  const char* fn = "mf_compress_blocks";
+}  // extern "C"
+
+namespace {
+
+mf_status compress_impl(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
+                        const float* row_lse, const float* block_mass, float tau, int32_t* row_ptr,
+                        int32_t* col_idx, void* values, int64_t capacity_blocks, int64_t* nnz_out,
+                        void* workspace, size_t workspace_bytes, void* stream, const char* fn) {
   mf_status st = check_sender(desc, batch, fn);
   if (st) return st;
   if (!(tau > 0.f && tau <= 1.f)) return fail(MF_ERR_INVALID, "%s: tau = %g not in (0, 1]", fn, (double)tau);
@@ -244,6 +247,66 @@ mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch, 
   x.scale = scale_of(desc);
   e = mf::launch_extract(x, desc->dtype, stream);
   return e ? hip_fail(e, fn) : MF_OK;
+}
+
+// The no-allocation variant's scratch: one array per device, holding the
+// selection's per-row counts and keep bits and the scan's total.  Host code
+// reaches it only through the address hipGetSymbolAddress returns on each
+// device (the array's name is a host-side stand-in).
+constexpr size_t kStaticScratchBytes = (size_t)MF_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch's device address on the current device (set up once per device)
+mf_status static_scratch(void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail((int)e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(MF_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol, fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch, const void* q, const void* k,
+                             const float* row_lse, const float* block_mass, float tau, int32_t* row_ptr,
+                             int32_t* col_idx, void* values, int64_t capacity_blocks, int64_t* nnz_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mf::clear_error();
+  return compress_impl(desc, batch, q, k, row_lse, block_mass, tau, row_ptr, col_idx, values, capacity_blocks,
+                       nnz_out, workspace, workspace_bytes, stream, "mf_compress_blocks");
+}
+
+mf_status mf_compress_blocks_noalloc(const mf_sender_desc* desc, const mf_batch* batch, const void* q,
+                                     const void* k, const float* row_lse, const float* block_mass, float tau,
+                                     int32_t* row_ptr, int32_t* col_idx, void* values, int64_t capacity_blocks,
+                                     int64_t* nnz_out, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_compress_blocks_noalloc";
+  mf_status st = check_sender(desc, batch, fn);
+  if (st) return st;
+  const size_t need = workspace_layout(desc, batch).bytes;
+  if (need > kStaticScratchBytes)
+    return fail(MF_ERR_WORKSPACE, "%s: needs %zu bytes of scratch, the static scratch holds %zu", fn, need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws, fn);
+  if (st) return st;
+  return compress_impl(desc, batch, q, k, row_lse, block_mass, tau, row_ptr, col_idx, values, capacity_blocks,
+                       nnz_out, ws, kStaticScratchBytes, stream, fn);
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_map_cache_destroy", "mf_map_cache_insert", "mf_map_cache_lookup", "mf_map_cache_release",
            "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_headmix_workspace_size", "mf_headmix_gram",
            "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version",
-           "mf_debug_force_portable")
+           "mf_debug_force_portable", "mf_compress_blocks_noalloc")
 # stages mf_debug_force_portable can send to their portable twins
 FORCE_PORTABLE = {"stats": 0x1, "select": 0x2, "extract": 0x4, "mapped": 0x8}
 
@@ -116,6 +116,8 @@ def lib():
     L.mf_compress_workspace_size.restype = sz
     L.mf_compress_blocks.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
                                      ctypes.c_float, vp, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
+    L.mf_compress_blocks_noalloc.argtypes = [ctypes.POINTER(SenderDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp, vp, i64, ctypes.POINTER(i64), vp]
     L.mf_mapped_attn_v.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
                                    vp, vp, vp]
     L.mf_mapped_attn_v_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(ReceiverDesc)), ctypes.c_int,
@@ -277,6 +279,23 @@ def compress_blocks(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, t
                                   ws_bytes, _stream(stream))
     _check(st)
     return int(nnz.value) if sync_count else None
+
+
+def compress_blocks_noalloc(desc: SenderDesc, batch: Batch, q, k, row_lse, block_mass, tau: float,
+                            row_ptr, col_idx, values, capacity: int, sync_count: bool = True,
+                            stream=None) -> Optional[int]:
+    """compress_blocks without a workspace: the library's static per-GPU
+    scratch stands in for it (calls that overlap on one GPU race)."""
+    nnz = ctypes.c_int64(-1)
+    st = lib().mf_compress_blocks_noalloc(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(q), _ptr(k),
+                                          _ptr(row_lse), _ptr(block_mass), float(tau), _ptr(row_ptr),
+                                          _ptr(col_idx), _ptr(values), int(capacity),
+                                          ctypes.byref(nnz) if sync_count else None, _stream(stream))
+    _check(st)
+    return int(nnz.value) if sync_count else None
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # MF_STATIC_SCRATCH_BYTES
 
 
 def receiver_desc(v: torch.Tensor, H_s: int, H_r: int, d: int, B: int, layer_map: Sequence[int],

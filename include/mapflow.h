@@ -194,6 +194,23 @@ mf_status mf_compress_blocks(const mf_sender_desc* desc, const mf_batch* batch,
                              int64_t capacity_blocks, int64_t* nnz_out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* mf_compress_blocks for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, whose role a static
+ * device array of MF_STATIC_SCRATCH_BYTES per GPU takes (held by each GPU the
+ * library runs on until the process ends).  It calls no allocator.  A batch
+ * whose mf_compress_workspace_size() exceeds MF_STATIC_SCRATCH_BYTES returns
+ * MF_ERR_WORKSPACE before anything is launched.  Every call on one GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU race; calls in
+ * one stream, or separated by synchronisation, do not.  The array's contents
+ * on entry do not matter. */
+#define MF_STATIC_SCRATCH_BYTES (16u << 20)
+mf_status mf_compress_blocks_noalloc(const mf_sender_desc* desc, const mf_batch* batch,
+                                     const void* q, const void* k,
+                                     const float* row_lse, const float* block_mass, float tau,
+                                     int32_t* row_ptr, int32_t* col_idx, void* values,
+                                     int64_t capacity_blocks, int64_t* nnz_out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Receiver side: fused mapped attention . V                                */
 /* ------------------------------------------------------------------------ */
