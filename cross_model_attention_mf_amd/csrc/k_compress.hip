@@ -570,6 +570,169 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
   }
 }
 
+
+// 128-row blocks: the same scheme over 64-key halves.  A workgroup walks its
+// row-block's kept 128-key blocks one 64-key half at a time (the K ring holds
+// 64-key stages); for each half, wave w computes rows 64 a + 32 (w % 2) ..
+// + 31 against keys 32 (w / 2) .. + 31 of the half for both 64-row halves a,
+// so every K fragment feeds two MFMA chains.  The half's 64 keys x 128 rows
+// go through a key-major LDS tile to 256-byte rows of the value block.
+constexpr int XPITCH2 = 128 * 2 + 16;   // bytes per key row of the 128-row output tile
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int STAGE = 64 * ROWB;
+  constexpr int CPW = STAGE / 1024 / 4;
+  constexpr int BB = 128;
+  extern __shared__ __align__(16) char ring[];
+  __shared__ __align__(16) char otile[64 * XPITCH2];
+  __shared__ int jlist[kXMaxCb];
+  __shared__ int nkept;
+
+  int rb, h, l;
+  xcd_unflatten(blockIdx.x, a.b.total_rb, a.H, a.L, rb, h, l);
+  if (l >= a.L) return;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, BB, rb);
+  const size_t lh = (size_t)l * a.H + h;
+  const size_t row = lh * a.b.total_rb + rb;
+  const int64_t base = a.row_ptr[row];
+  const int hk = h / (a.H / a.Hkv);
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qh = w & 1, kh = w >> 1;
+
+  // Q rows 64 a + 32 qh + L % 32 as A operands and lse2 of the lane's output
+  // rows of both halves
+  const float c2 = (float)(a.scale * kLog2eD);
+  bf16x8 qf[2][KS];
+  float lse2[2][16];
+  {
+    const float* __restrict__ lrow = a.row_lse + lh * a.b.total_q + ri.q0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 64 * hf + 32 * qh + l32;
+      const bf16* src = reinterpret_cast<const bf16*>(a.q) + (size_t)l * a.lsq +
+                        ((size_t)(ri.q0 + (r < ri.rows ? r : 0)) * a.H + h) * D + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[hf][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 64 * hf + 32 * qh + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const float v = lrow[rr < ri.rows ? rr : 0];
+        lse2[hf][e] = rr < ri.rows ? v * kLog2e : INFINITY;
+      }
+    }
+  }
+
+  // kept column blocks, as in the 64-row kernel
+  if (w == 0) {
+    const uint32_t bw = lane < a.words ? a.keep_bits[row * (size_t)a.words + lane] : 0u;
+    const int cnt = __popc(bw);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    uint32_t bits = bw;
+    while (bits) {
+      const int j = lane * 32 + __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (base + pos < a.capacity) a.col_idx[base + pos] = j;
+      jlist[pos++] = j;
+    }
+    if (lane == 63) {
+      const int64_t room = a.capacity - base;
+      nkept = a.values ? (int)(room < 0 ? 0 : (room < incl ? room : incl)) : 0;
+    }
+  }
+  __syncthreads();
+  const int n = __builtin_amdgcn_readfirstlane(nkept);
+  if (n == 0) return;
+
+  const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)l * a.lsk +
+                                   (size_t)ri.k0 * a.Hkv * D + (size_t)hk * D;
+  const size_t kstride = (size_t)a.Hkv * D;
+  const int klast = ri.klen - 1;
+  // stage t: key half t % 2 of kept block t / 2
+  auto issue = [&](int t) {
+    const int tt = t < 2 * n ? t : 2 * n - 1;
+    const int j = __builtin_amdgcn_readfirstlane(jlist[tt >> 1]);
+    char* stage = ring + (t % XNST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int pidx = (i * 4 + w) * 64 + lane;
+      const int key = pidx / CPR, cc = pidx % CPR;
+      const int src_chunk = cc ^ (key & (CPR - 1));
+      const int kabs = min(j * BB + 64 * (tt & 1) + key, klast);
+      xcopy16(kbase + (size_t)kabs * kstride + src_chunk * 8, stage + (i * 4 + w) * 1024);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < XNST - 1; ++t) issue(t);
+
+  const int diag = ri.ncand - 1;
+  bf16* __restrict__ vals = reinterpret_cast<bf16*>(a.values);
+
+  for (int t = 0; t < 2 * n; ++t) {
+    switch (min(t, XNST - 1)) {
+      case 0: xwait_vmcnt<(XNST - 2) * CPW + 0>(); break;
+      case 1: xwait_vmcnt<(XNST - 2) * CPW + 2>(); break;
+      default: xwait_vmcnt<(XNST - 2) * CPW + 4>(); break;
+    }
+    __syncthreads();
+    issue(t + XNST - 1);
+    const char* stage = ring + (t % XNST) * STAGE;
+    const int kb = t & 1;                    // key half of the block
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const int key = 32 * kh + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int chunk = (2 * ks + hi) ^ (key & (CPR - 1));
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + key * ROWB + chunk * 16);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][ks], kf, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][ks], kf, acc[1], 0, 0, 0);
+    }
+    // causal mask (diagonal block only: key 64 kb + key against row 64 a + r)
+    // and rows past the row-block (lse2 = inf)
+    const bool dg = jlist[t >> 1] == diag;
+    const int kr = 64 * kb + key;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          const int r = 64 * hf + 32 * qh + 8 * g + 4 * hi + i;
+          float x = __builtin_amdgcn_exp2f(fmaf(acc[hf][e], c2, -lse2[hf][e]));
+          if (dg && kr > r) x = 0.f;
+          p[i] = x;
+        }
+        const int r0 = 64 * hf + 32 * qh + 8 * g + 4 * hi;
+        uint2 pk;
+        pk.x = pack_bf16x2(p[0], p[1]);
+        pk.y = pack_bf16x2(p[2], p[3]);
+        *reinterpret_cast<uint2*>(otile + key * XPITCH2 + r0 * 2) = pk;
+      }
+    __syncthreads();
+    // 64 key rows of 256 bytes: key 64 kb + kk of value block t / 2
+    bf16* dst = vals + (size_t)(base + (t >> 1)) * BB * BB + (size_t)(64 * kb) * BB;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = c * 256 + tid;          // 16-byte chunk: key ch / 16, rows 8 (ch % 16) ..
+      const int kk = ch >> 4, part = ch & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(otile + kk * XPITCH2 + part * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * BB + part * 8));
+    }
+  }
+}
+
 template <typename T, int B, int D>
 int launch_ex(const ExtractArgs& a, void* stream) {
   dim3 grid(xcd_grid(a.b.total_rb, a.H, a.L));
@@ -627,7 +790,7 @@ int launch_scan(const ScanArgs& a, void* stream) {
 }
 
 bool extract_fast_path(mf_dtype dt, int B, int d) {
-  if (dt != MF_BF16 || B != 64 || (d != 64 && d != 128)) return false;
+  if (dt != MF_BF16 || (B != 64 && B != 128) || (d != 64 && d != 128)) return false;
   return !(forced_portable() & MF_FORCE_PORTABLE_EXTRACT);
 }
 
@@ -637,7 +800,8 @@ int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream) {
   if (a.b.total_rb == 0 || a.L == 0) return 0;
   if (a.values && a.words <= 64 && extract_fast_path(dt, a.B, a.d)) {
     const size_t lds = extract_mfma_lds_bytes(a.d);
-    auto kern = a.d == 128 ? extract_mfma_kernel<128> : extract_mfma_kernel<64>;
+    auto kern = a.B == 128 ? (a.d == 128 ? extract_mfma128_kernel<128> : extract_mfma128_kernel<64>)
+                           : (a.d == 128 ? extract_mfma_kernel<128> : extract_mfma_kernel<64>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(kern, dim3(xcd_grid(a.b.total_rb, a.H, a.L)), dim3(256), lds, (hipStream_t)stream, a);

@@ -221,21 +221,23 @@ __device__ __forceinline__ float swap32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Group leaders: row-block rb leads a group when it is the first, fifth, ...
-// row-block of its sequence.  One workgroup of 1024 threads writes the
-// leaders in ascending order, their count, and clears the per-XCD queues.
-__global__ void __launch_bounds__(1024) stats_groups_kernel(BatchArgs b, int32_t* hdr, int32_t* table) {
+// Group leaders over 64-row units (unit u is half u % sub of row-block
+// u / sub; sub = B / 64): unit u leads a group when it is the first, fifth,
+// ... unit of its sequence.  One workgroup of 1024 threads writes the leaders
+// in ascending order, their count, and clears the per-XCD queues.
+__global__ void __launch_bounds__(1024) stats_groups_kernel(BatchArgs b, int sub, int32_t* hdr, int32_t* table) {
   __shared__ int wcount[16];
   __shared__ int base;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (tid == 0) base = 0;
   __syncthreads();
-  for (int c0 = 0; c0 < b.total_rb; c0 += 1024) {
+  const int nunits = b.total_rb * sub;
+  for (int c0 = 0; c0 < nunits; c0 += 1024) {
     const int rb = c0 + tid;
     bool lead = false;
-    if (rb < b.total_rb) {
-      const int s = b.plan[b.num_seqs + 1 + rb];
-      lead = ((rb - b.plan[s]) % SQ) == 0;
+    if (rb < nunits) {
+      const int s = b.plan[b.num_seqs + 1 + rb / sub];
+      lead = ((rb - sub * b.plan[s]) % SQ) == 0;
     }
     const unsigned long long m = __ballot(lead);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
@@ -256,7 +258,23 @@ __global__ void __launch_bounds__(1024) stats_groups_kernel(BatchArgs b, int32_t
   if (tid == 0) hdr[kXcds] = base;
 }
 
-template <int D>
+// 64-row unit u of a batch of SUB * 64-row row-blocks: half u % SUB of
+// row-block u / SUB, with its own rows, positions and 64-key causal range
+// (rows = 0 for the empty second half of a short last row-block)
+template <int SUB>
+__device__ __forceinline__ RowBlockInfo unit_info(const BatchArgs& b, int u) {
+  RowBlockInfo r = rowblock_info(b.plan, b.num_seqs, b.cu_q, b.cu_k, b.q_pos0, 64 * SUB, u / SUB);
+  if constexpr (SUB > 1) {
+    const int half = u % SUB;
+    r.q0 += 64 * half;
+    r.pos0 += 64 * half;
+    r.rows = max(0, min(64, r.rows - 64 * half));
+    r.ncand = r.rows > 0 ? (r.pos0 + r.rows - 1) / 64 + 1 : 0;
+  }
+  return r;
+}
+
+template <int D, int SUB>
 __global__ void __launch_bounds__(SQ * 64, 2)
 stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, float* __restrict__ escratch) {
   constexpr int KS = D / 16;            // MFMA k-steps over the head dim
@@ -277,7 +295,8 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
   const long long nitems = npx * ngroups;
   const float c2 = (float)(a.scale * kLog2eD);
   const double c2d = a.scale * kLog2eD;
-  float* __restrict__ ew = escratch + ((size_t)blockIdx.x * SQ + w) * 64 * a.b.max_cb;  // [block][row]
+  const int max_cb64 = a.b.max_cb * SUB;   // 64-key blocks
+  float* __restrict__ ew = escratch + ((size_t)blockIdx.x * SQ + w) * 64 * max_cb64;  // [block][row]
   const size_t kstride = (size_t)a.Hkv * D;
 
   for (;;) {
@@ -292,14 +311,14 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
     const int lead = table[ngroups - 1 - (int)(item % ngroups)];
     const int l = (int)(p / a.H), h = (int)(p % a.H);
     const int hk = h / (a.H / a.Hkv);
-    const int seq = a.b.plan[a.b.num_seqs + 1 + lead];
-    const int last_rb = min(lead + SQ - 1, a.b.plan[seq + 1] - 1);
-    const RowBlockInfo rlast = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, 64, last_rb);
+    const int seq = a.b.plan[a.b.num_seqs + 1 + lead / SUB];
+    int last_rb = min(lead + SQ - 1, SUB * a.b.plan[seq + 1] - 1);
+    RowBlockInfo rlast = unit_info<SUB>(a.b, last_rb);
+    if (SUB > 1 && rlast.rows == 0) rlast = unit_info<SUB>(a.b, --last_rb);   // empty second half
     const int jtop = rlast.ncand - 1;
     const int rb = lead + w;
     const bool valid = rb <= last_rb;
-    const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, 64,
-                                          valid ? rb : last_rb);
+    const RowBlockInfo ri = unit_info<SUB>(a.b, valid ? rb : last_rb);
     const int diag = valid ? ri.ncand - 1 : -1;
 
     const bf16* __restrict__ kbase = reinterpret_cast<const bf16*>(a.k) + (size_t)l * a.lsk +
@@ -481,6 +500,9 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
 
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the K ring: LDS becomes the transposes
+    // 128-row blocks: row sums of each 64-key block of the wave's half, in
+    // LDS after the transposes, combined below by the first half's wave
+    float* const hsum = reinterpret_cast<float*>(smem) + SQ * 64 * SEPITCH + (size_t)w * max_cb64;
     if (valid) {
       // lane L keeps query row L: half L / 32 of the wave's two 32-row halves
       const float mr = hi ? m_ref[1] : m_ref[0];
@@ -491,7 +513,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       if (lane < ri.rows)
         a.row_lse[lh * a.b.total_q + ri.q0 + lane] = (float)((double)mr * a.scale + lse2 * kLn2);
       float* tr = reinterpret_cast<float*>(smem) + w * 64 * SEPITCH;
-      float* __restrict__ bm = a.block_mass + (lh * a.b.total_rb + rb) * (size_t)a.b.max_cb;
+      float* __restrict__ bm = a.block_mass + (lh * a.b.total_rb + rb) * (size_t)a.b.max_cb;   // SUB == 1
       for (int j0 = 0; j0 < ri.ncand; j0 += 64) {
         const int nj = min(64, ri.ncand - j0);
         // the scratch rows were written by this wave on this CU and its
@@ -508,11 +530,40 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         if (lane < nj) {
           double accm = 0.0;
           for (int r = 0; r < ri.rows; ++r) accm += (double)tr[lane * SEPITCH + r];
-          bm[j0 + lane] = (float)(accm / ri.rows);
+          if constexpr (SUB == 1) bm[j0 + lane] = (float)(accm / ri.rows);
+          else hsum[j0 + lane] = (float)accm;
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       }
-      for (int j = ri.ncand + lane; j < a.b.max_cb; j += 64) bm[j] = 0.f;
+      if constexpr (SUB == 1)
+        for (int j = ri.ncand + lane; j < a.b.max_cb; j += 64) bm[j] = 0.f;
+    }
+    if constexpr (SUB == 2) {
+      // a half's sums past its own causal range are 0 (the first half sees
+      // one 64-key block fewer of the diagonal 128-key block, an empty half none)
+      if (valid)
+        for (int j = ri.ncand + lane; j < max_cb64; j += 64) hsum[j] = 0.f;
+      __syncthreads();
+      if ((w & 1) == 0 && valid) {
+        // the row-block's masses: both halves' sums over both 64-key halves
+        // of each 128-key block, over the row-block's rows
+        const int rb128 = rb / 2;
+        const bool second = rb + 1 <= last_rb;
+        const RowBlockInfo r2 = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, 128, rb128);
+        const size_t lh = (size_t)l * a.H + h;
+        float* __restrict__ bm = a.block_mass + (lh * a.b.total_rb + rb128) * (size_t)a.b.max_cb;
+        const float* hs2 = hsum + max_cb64;
+        for (int J = lane; J < a.b.max_cb; J += 64) {
+          float m = 0.f;
+          if (J < r2.ncand) {
+            double t = (double)hsum[2 * J] + (double)hsum[2 * J + 1];
+            if (second) t += (double)hs2[2 * J] + (double)hs2[2 * J + 1];
+            m = (float)(t / r2.rows);
+          }
+          bm[J] = m;
+        }
+      }
+      __syncthreads();   // the sums are read before the next item's ring overwrites LDS
     }
   }
 }
@@ -525,23 +576,26 @@ size_t block_stats_lds_bytes(int B, int max_cb) {
 }
 
 bool stats_fast_path(mf_dtype dt, int B, int d) {
-  if (dt != MF_BF16 || B != 64 || (d != 64 && d != 128)) return false;
+  if (dt != MF_BF16 || (B != 64 && B != 128) || (d != 64 && d != 128)) return false;
   return !(forced_portable() & MF_FORCE_PORTABLE_STATS);
 }
 
-static size_t stats_mfma_lds_bytes(int d) {
+static size_t stats_mfma_lds_bytes(int d, int B, int max_cb) {
   const size_t ring = (size_t)SNST * 64 * d * 2;
-  const size_t tr = (size_t)SQ * 64 * SEPITCH * 4;
+  // 128-row blocks: the halves' row sums per 64-key block beside the transposes
+  const size_t tr = (size_t)SQ * 64 * SEPITCH * 4 + (B == 128 ? (size_t)SQ * 2 * max_cb * 4 : 0);
   return ring > tr ? ring : tr;
 }
 
 StatsWorkspace stats_workspace_layout(int B, int max_cb, int total_rb, int slots) {
+  // 64-row units: B / 64 per row-block, each with B / 64 times the 64-key blocks
+  const size_t sub = (size_t)B / 64;
   StatsWorkspace w;
   w.hdr = 0;
   w.table = 256;
-  w.escratch = w.table + ((size_t)total_rb * 4 + 255) / 256 * 256;
+  w.escratch = w.table + ((size_t)total_rb * sub * 4 + 255) / 256 * 256;
   w.slots = slots;
-  w.bytes = w.escratch + (size_t)slots * SQ * B * (size_t)max_cb * 4;
+  w.bytes = w.escratch + (size_t)slots * SQ * 64 * (size_t)max_cb * sub * 4;
   return w;
 }
 
@@ -554,11 +608,13 @@ int launch_block_stats(const StatsArgs& a, mf_dtype dt, void* stream) {
     int32_t* hdr = reinterpret_cast<int32_t*>(ws + a.wsl.hdr);
     int32_t* table = reinterpret_cast<int32_t*>(ws + a.wsl.table);
     float* escr = reinterpret_cast<float*>(ws + a.wsl.escratch);
-    hipLaunchKernelGGL(stats_groups_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, a.b, hdr, table);
+    const int sub = a.B / 64;
+    hipLaunchKernelGGL(stats_groups_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, a.b, sub, hdr, table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    const size_t lds = stats_mfma_lds_bytes(a.d);
-    auto kern = a.d == 128 ? stats_mfma_kernel<128> : stats_mfma_kernel<64>;
+    const size_t lds = stats_mfma_lds_bytes(a.d, a.B, a.b.max_cb);
+    auto kern = sub == 2 ? (a.d == 128 ? stats_mfma_kernel<128, 2> : stats_mfma_kernel<64, 2>)
+                         : (a.d == 128 ? stats_mfma_kernel<128, 1> : stats_mfma_kernel<64, 1>);
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(kern, dim3(a.wsl.slots), dim3(SQ * 64), lds, (hipStream_t)stream, a, hdr, table, escr);

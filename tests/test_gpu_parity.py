@@ -218,13 +218,17 @@ def test_portable_and_mfma_mapped_kernels_agree_with_oracle(B, d, Hs, Hr, Hkv):
     assert torch.allclose(runs[0], runs[1], rtol=2e-2, atol=2e-2 * float(runs[0].abs().max()))
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_portable_and_mfma_block_stats_agree_with_oracle(d):
+@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_portable_and_mfma_block_stats_agree_with_oracle(B, d):
     # varlen chunked batch: groups of four row-blocks cut short by sequence
     # ends, a one-row tail block, a sequence shorter than one block, several
-    # (layer, head) pairs per XCD queue, and chunk rows starting past 0
-    wl = tiny_structured("bf16", workload_id=15, B=64, d=d, H_s=12, H_r=4, num_layers=2,
-                         seqlens=(64 * 9 + 17, 64 * 2 + 1, 63, 64 * 5, 700), chunk=256)
+    # (layer, head) pairs per XCD queue, and chunk rows starting past 0; at
+    # B = 128 also last row-blocks whose second 64-row half is empty (1, 17,
+    # 60 and 64 rows) or partial (100 rows)
+    seqlens = ((64 * 9 + 17, 64 * 2 + 1, 63, 64 * 5, 700) if B == 64 else
+               (128 * 5 + 17, 128 + 1, 63, 128 * 3 + 64, 700, 128 * 2 + 100))
+    wl = tiny_structured("bf16", workload_id=15, B=B, d=d, H_s=12, H_r=4, num_layers=2,
+                         seqlens=seqlens, chunk=256)
     results = []
     for stages in (("stats",), ()):
         with mf.force_portable(*stages):
@@ -258,13 +262,13 @@ def test_wave_and_workgroup_selection_agree(B, seqlens):
         assert torch.equal(a.state.values, b.state.values)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_portable_and_mfma_extraction_agree_with_oracle(d):
-    """bf16, B = 64: the MFMA extraction and its portable twin write the same
-    CSR; their values (each rounded to bf16 from its own fp32 scores) agree to
-    a bf16 rounding step, and both match the oracle."""
-    wl = tiny_structured("bf16", workload_id=17, B=64, d=d, H_s=6, H_r=4,
-                         seqlens=(64 * 5 + 9, 64 * 2, 33), chunk=None)
+@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_portable_and_mfma_extraction_agree_with_oracle(B, d):
+    """bf16: the MFMA extraction and its portable twin write the same CSR;
+    their values (each rounded to bf16 from its own fp32 scores) agree to a
+    bf16 rounding step, and both match the oracle."""
+    wl = tiny_structured("bf16", workload_id=17, B=B, d=d, H_s=6, H_r=4,
+                         seqlens=(B * 5 + 9, B * 2, 33, B + 70), chunk=None)
     runs = []
     for stages in (("extract",), ()):
         with mf.force_portable(*stages):
