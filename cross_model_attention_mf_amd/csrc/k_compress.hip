@@ -379,14 +379,21 @@ __global__ void __launch_bounds__(B * 4) extract_kernel(ExtractArgs a) {
 // the four consecutive rows 8 (e / 4) + 4 (L / 32) + 0..3 of register group
 // e / 4, so exp2(s c2 - lse2) of four rows packs into one 8-byte bf16 LDS
 // write of the key-major tile; the workgroup then stores the 8 KB tile with
-// 16-byte vector stores.  The ring has two slots and, for head dim 128, the
-// tile is written into the slot whose K the block just consumed: about 35 KB
-// of LDS and 128 VGPRs let four workgroups share a CU, and that occupancy
-// hides the K fetches better than a deeper ring.
+// 16-byte vector stores.  The ring has two slots and the tile is written
+// into the slot whose K the block just consumed: at most 32 KB of LDS and 128
+// VGPRs let four workgroups share a CU, and that occupancy hides the K
+// fetches better than a deeper ring.
 // ---------------------------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int XNST = 2;                 // K ring depth
-constexpr int XPITCH = 64 * 2 + 16;     // bytes per key row of the output tile (16-byte aligned)
+// Output tile [64 keys][64 rows] bf16, 128 bytes per key row, 16-byte chunk c
+// of key k stored at chunk c ^ ((k / 2) % 8).  A write instruction (32 keys x
+// 8 bytes per half-wave) then spreads over every bank, and so does a
+// read-back quarter-wave (two key rows of 128 bytes, in opposite bank halves).
+constexpr int XPITCH = 64 * 2;
+__device__ __forceinline__ int xtile_off(int key, int byte) {   // byte < 128
+  return key * XPITCH + ((((byte >> 4) ^ ((key >> 1) & 7))) << 4) + (byte & 15);
+}
 constexpr int kXMaxCb = (MF_MAX_KEYS + 63) / 64;   // column blocks of the longest sequence
 
 // Async 16-byte-per-lane copy HBM -> LDS (lane L lands at base + 16 L).
@@ -553,7 +560,7 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
       uint2 pk;
       pk.x = pack_bf16x2(p[0], p[1]);
       pk.y = pack_bf16x2(p[2], p[3]);
-      *reinterpret_cast<uint2*>(ot + key * XPITCH + r0 * 2) = pk;
+      *reinterpret_cast<uint2*>(ot + xtile_off(key, r0 * 2)) = pk;
     }
     __syncthreads();
     // non-temporal stores: the values are read only by a later kernel, and
@@ -564,7 +571,7 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
     for (int c = 0; c < 2; ++c) {
       const int ch = c * 256 + tid;           // 16-byte chunk: key ch / 8, rows 8 (ch % 8) ..
       const int kk = ch >> 3, part = ch & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + kk * XPITCH + part * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + xtile_off(kk, part * 16));
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * 64 + part * 8));
     }
   }
@@ -577,7 +584,11 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
 // + 31 against keys 32 (w / 2) .. + 31 of the half for both 64-row halves a,
 // so every K fragment feeds two MFMA chains.  The half's 64 keys x 128 rows
 // go through a key-major LDS tile to 256-byte rows of the value block.
-constexpr int XPITCH2 = 128 * 2 + 16;   // bytes per key row of the 128-row output tile
+// 128-row output tile: 256 bytes per key row, chunk c of key k at c ^ (k % 16)
+constexpr int XPITCH2 = 128 * 2;
+__device__ __forceinline__ int xtile2_off(int key, int byte) {   // byte < 256
+  return key * XPITCH2 + ((((byte >> 4) ^ (key & 15))) << 4) + (byte & 15);
+}
 
 template <int D>
 __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) {
@@ -718,7 +729,7 @@ __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) 
         uint2 pk;
         pk.x = pack_bf16x2(p[0], p[1]);
         pk.y = pack_bf16x2(p[2], p[3]);
-        *reinterpret_cast<uint2*>(otile + key * XPITCH2 + r0 * 2) = pk;
+        *reinterpret_cast<uint2*>(otile + xtile2_off(key, r0 * 2)) = pk;
       }
     __syncthreads();
     // 64 key rows of 256 bytes: key 64 kb + kk of value block t / 2
@@ -727,7 +738,7 @@ __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) 
     for (int c = 0; c < 4; ++c) {
       const int ch = c * 256 + tid;          // 16-byte chunk: key ch / 16, rows 8 (ch % 16) ..
       const int kk = ch >> 4, part = ch & 15;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(otile + kk * XPITCH2 + part * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(otile + xtile2_off(kk, part * 16));
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * BB + part * 8));
     }
   }
