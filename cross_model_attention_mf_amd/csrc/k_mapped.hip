@@ -264,7 +264,7 @@ template <int B, int D, int HP, int KVC, int NS, int NVB>
 struct MapCfg {
   static_assert(B == 64 || B == 128, "64- or 128-row blocks");
   static_assert(HP % 16 == 0 && HP >= 16 && HP <= 64, "sender heads padded to 16");
-  static_assert(NS >= 2 && NS <= 5 && (NVB == 1 || NVB == 2), "ring plan");
+  static_assert(NS >= 2 && NS <= 8 && (NVB == 1 || NVB == 2), "ring plan");
   static constexpr int QH = B / kMapRows;            // workgroups per row-block
   static constexpr int SPB = B / 4;                  // 4-key stages per block
   static constexpr int SB = B / 16;                  // 16-key steps per block
@@ -299,11 +299,20 @@ struct MapCfg {
   // after the copies of stage p
   static constexpr int MC = 1 + B / 64;              // union-merge copies (next columns, page ids)
   static constexpr int ops(int p) { return PCW + (p == VPART ? VC : 0) + (p == 1 ? MC : 0); }
-  static constexpr int allow(int p) {
+  static constexpr int allow_p(int p) {
     int n = 0;
     for (int b = 1; b <= NS - 2; ++b) n += ops((p - b + 8) & 3);
     return n;
   }
+  // The first stage of a step also reads the previous step's V rows, issued
+  // at its stage VPART before that stage's merge copies and P: those and every
+  // later stage's copies may be in flight.
+  static constexpr int allow_v() {
+    int n = (VPART == 1 ? MC : 0) + PCW;
+    for (int q = VPART + 1; q <= 3; ++q) n += ops(q);
+    return n;
+  }
+  static constexpr int allow(int p) { return p == 0 && allow_v() < allow_p(0) ? allow_v() : allow_p(p); }
 };
 
 size_t map_lds_bytes(int B, int D, int HP, int KVC, int NS, int NVB) {
