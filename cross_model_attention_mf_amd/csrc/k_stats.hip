@@ -6,22 +6,31 @@
 // waves, each wave owning 16 query rows.  The row-block's causal column
 // blocks are visited once, diagonal block first, then 0 .. diag-1:
 //   S = Q_rows K_cols^T           bf16 MFMA 16x16x32 (fp32: 16x16x4), fp32 acc
-//   m_run = running row max       (m_ref = max of the diagonal block)
+//   m_run = running row max
 //   s_rj  = sum_c exp2((S - m_run) * c2)        c2 = scale * log2(e)
 //   E[r][j] = log2(s_rj) + (m_run - m_ref) * c2  (log2 mass relative to m_ref)
 //   l_run = online sum of the s_rj (fp64)
-// E lives in LDS (B x ncand floats).  Epilogue: per row
+// m_ref starts as the diagonal block's maximum; when m_run passes it by more
+// than kRebase log2 units the row's stored E move to m_ref = m_run (in fp64).
+// E thus stays below log2(B) + kRebase in magnitude wherever the mass is not
+// negligible, where the fp32 E (and the hardware log2) are good to ~1e-6
+// relative in the mass.  E lives in LDS (B x ncand floats).  Epilogue: per row
 //   lse2_r = (m_run - m_ref) * c2 + log2(l_run)     (fp64)
 //   row_lse_r = scale * m_ref + ln2 * lse2_r
 // and per column block, in fp64, mass_j = sum_r exp2(E[r][j] - lse2_r) / R.
-// Keeping E relative to the diagonal block's maximum keeps the important
-// blocks' log-masses small in magnitude, so fp32 holds them to ~1e-7.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace mf {
 
 namespace {
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+constexpr double kRebase = 8.0;
 
 template <typename T, int B, int D>
 __global__ void __launch_bounds__(B * 4)
@@ -102,7 +111,21 @@ block_stats_kernel(StatsArgs a) {
       } else {
         if (m_new > m_run[i]) l_run[i] *= (double)exp2f((m_run[i] - m_new) * c2);
         l_run[i] += (double)s;
-        Ev[i] = log2f(s) + (float)(((double)m_new - (double)m_ref[i]) * c2d);
+        double off = ((double)m_new - (double)m_ref[i]) * c2d;
+        if (off > kRebase) {
+          // the row's earlier blocks (the diagonal, then 0 .. j - 1), written
+          // by this lane, move to the new reference
+          if (lr == i && rowok[i]) {
+            float* Er = E + (size_t)rowl[i] * ecols;
+            for (int tp = 0; tp < t; ++tp) {
+              float* e = Er + (tp == 0 ? diag : tp - 1);
+              *e = (float)((double)*e - off);
+            }
+          }
+          m_ref[i] = m_new;
+          off = 0.0;
+        }
+        Ev[i] = log2f(s) + (float)off;
       }
       m_run[i] = m_new;
     }
@@ -179,12 +202,16 @@ int launch_d(const StatsArgs& a, void* stream) {
 // query L % 32 of each 32-query half and 16 keys of each 32-key tile, so a
 // row max / row sum over a 64-key block is an in-lane reduction plus one
 // v_permlane32_swap with lane L ^ 32.  Only the diagonal block takes a row
-// max: it is the exponent reference of every later block of the row, whose
-// sums are taken against it directly (a block that would overflow that
-// reference is re-taken against its own maximum).  Each block's log2 mass relative to
-// m_ref goes to a per-slot scratch table in HBM ([block][row], one coalesced
-// 256-byte store per wave and block); the epilogue reads it back through LDS
-// transposes and sums the masses in fp64.  The grid is persistent: slot b
+// max: it is the exponent reference m_run of every later block of the row,
+// whose sums are taken against it directly; a 32-key half with a score more
+// than 13 log2 units above it moves m_run to the half's maximum and is taken
+// again.  Off the diagonal a block runs in two 32-key halves, software-
+// pipelined so that the matrix pipe computes one half's scores while the
+// vector pipe sums the half before it.  Each block's log2 mass relative to
+// m_run goes to a per-slot scratch table in HBM ([block][row], one coalesced
+// 256-byte store per wave and block; when m_run moves, the wave shifts the
+// entries it already stored, in fp64); the epilogue reads it back through
+// LDS transposes and sums the masses in fp64.  The grid is persistent: slot b
 // runs on XCD b % 8, takes (layer, head) pairs p = XCD, XCD + 8, ... from
 // its XCD's queue (heaviest row-block groups of a pair first), so the K of a
 // head stays in one XCD's L2.
@@ -198,11 +225,24 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, char* lds_generic_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)((uintptr_t)lds_generic_base), 16, 0, 0);
 }
+// 16 bytes per lane from a scalar base plus a 32-bit lane offset into LDS at
+// m0 + 16 * lane.  Inline assembly (the compiler neither counts it nor
+// orders LDS accesses against it beyond the memory clobber: the kernel's own
+// counted waits and barriers do); one wait state between the M0 write and
+// the copy reading it.
+__device__ __forceinline__ void copy16_saddr(unsigned voff, const void* sbase, unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ unsigned lds_addr(const char* lds_generic) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic);
 }
 
 // a copy of a lane value the compiler cannot see through
@@ -326,10 +366,11 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
     const int klast = rlast.klen - 1;
 
     // copies of column block jtop - t into ring slot t % SNST (steps past the
-    // end re-read block 0 so every wave issues the same number of copies)
-    // copy slot i of this wave: key kkey[i] of the block, source chunk
-    // csrc[i]; its source for block jb is kptr[i] + jb * 64 rows
-    const bf16* kptr[CPW];
+    // end re-read block 0 so every wave issues the same number of copies).
+    // Copy i of this wave: key kkey[i] of the block, source chunk
+    // cc ^ (key % CPR) at byte offset koff[i] from the block's first key row,
+    // whose address is scalar.
+    unsigned koff[CPW];
     int kkey[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -337,21 +378,22 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       const int key = pidx / CPR, cc = pidx % CPR;
       const int src_chunk = cc ^ (key & (CPR - 1));
       kkey[i] = key;
-      kptr[i] = kbase + (size_t)key * kstride + src_chunk * 8;
+      koff[i] = (unsigned)(((size_t)key * kstride + src_chunk * 8) * 2);
     }
+    const char* kbytes = reinterpret_cast<const char*>(kbase);
     auto issue = [&](int t) {
       const int jb = max(jtop - t, 0);
-      char* stage = smem + (t % SNST) * STAGE;
+      const char* src = kbytes + (size_t)jb * 64 * kstride * 2;
+      const unsigned m0 = lds_addr(smem + (t % SNST) * STAGE + w * 1024);
       if (jb * 64 + 63 <= klast) {
-        const size_t step = (size_t)jb * 64 * kstride;
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) copy16_to_lds(kptr[i] + step, stage + (i * SQ + w) * 1024);
+        for (int i = 0; i < CPW; ++i) copy16_saddr(koff[i], src, m0 + i * SQ * 1024);
       } else {
         // block reaching past the last key: clamp rows to the last key
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
           const int over = max(jb * 64 + kkey[i] - klast, 0);
-          copy16_to_lds(kptr[i] + ((size_t)jb * 64 - over) * kstride, stage + (i * SQ + w) * 1024);
+          copy16_saddr(koff[i] - (unsigned)((size_t)over * kstride * 2), src, m0 + i * SQ * 1024);
         }
       }
     };
@@ -378,12 +420,154 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
     }
 
     float m_ref[2] = {0.f, 0.f}, m_run[2] = {0.f, 0.f};
-    // (m_run - m_ref) c2 in log2 units, rounded once from fp64; it changes
-    // only when a block overflows the reference
-    float eoff[2] = {0.f, 0.f};
     double l_run[2] = {1.0, 1.0};
 
-    for (int t = 0; t <= jtop; ++t) {
+    // K fragment (kt, ks) of lane L in the block staged at `stage`: key
+    // 32 kt + L % 32, head-dim slice 16 ks + 8 (L / 32), at kfo[ks] +
+    // 32 kt ROWB (key % CPR, which picks the chunk swizzle, is the same for
+    // both kt), so with the stage's slot known at compile time each read is
+    // one LDS instruction with an immediate offset
+    // (opaque, so that the compiler keeps the KS sums instead of re-adding
+    // their common part at every read)
+    typedef __attribute__((address_space(3))) const char lds_char;
+    int kfo[KS];   // LDS byte addresses
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kfo[ks] = opaque_int((int)lds_addr(smem) + l32 * ROWB + (((2 * ks + hi) ^ (l32 & (CPR - 1))) * 16));
+    // soff: the stage's byte offset in the ring
+    auto kfrag = [&](int soff, int kt, int ks) {
+      lds_char* p = reinterpret_cast<lds_char*>((uintptr_t)(unsigned)kfo[ks]);
+      return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(p + soff + 32 * kt * ROWB);
+    };
+    // transposed scores of the 32-key half kt of a block:
+    // acc[kt][qt] = K[32 kt .. + 31] Q[32 qt .. + 31]^T
+    f32x16 acc[2][2];
+    auto mfma_half = [&](int soff, int kt) __attribute__((always_inline)) {
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = kfrag(soff, kt, ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc[kt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[0][ks], ks ? acc[kt][0] : f32x16{}, 0, 0, 0);
+        acc[kt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[1][ks], ks ? acc[kt][1] : f32x16{}, 0, 0, 0);
+      }
+    };
+    // in-lane sums of exp2(s c2 - nb) over half kt's 16 keys of each query
+    // tile (the lane's partner L ^ 32 holds the other 16)
+    auto half_sum = [&](int kt, const float (&nb)[2], float (&part)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float a0 = __builtin_amdgcn_exp2f(fmaf(acc[kt][qt][0], c2, -nb[qt]));
+        float a1 = __builtin_amdgcn_exp2f(fmaf(acc[kt][qt][1], c2, -nb[qt]));
+#pragma unroll
+        for (int e = 2; e < 16; e += 2) {
+          a0 += __builtin_amdgcn_exp2f(fmaf(acc[kt][qt][e], c2, -nb[qt]));
+          a1 += __builtin_amdgcn_exp2f(fmaf(acc[kt][qt][e + 1], c2, -nb[qt]));
+        }
+        part[qt] = a0 + a1;
+      }
+    };
+    // The MFMAs of half km of the block in `stage` on the matrix pipe while
+    // the vector pipe sums half kv of the scores already in acc: each MFMA is
+    // issued with the fma, exp2 and add of 16 / KS of those scores, and a
+    // scheduling barrier after each such group keeps that order.  The sums
+    // run in half_sum's order, so both give the same bits.
+    auto pipe_half = [&](int soff, int km, int kv, const float (&nb)[2], float (&part)[2]) __attribute__((always_inline)) {
+      constexpr int SPG = 16 / KS;   // scores summed per MFMA
+      static_assert(SPG * KS == 16 && SPG % 2 == 0, "two sum chains per query tile");
+      // K fragments read two k-steps ahead of the MFMAs using them
+      bf16x8 kf0 = kfrag(soff, km, 0), kf1 = kfrag(soff, km, 1);
+      float a[2][2];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf2 = ks + 2 < KS ? kfrag(soff, km, ks + 2) : kf0;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          acc[km][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[qt][ks], ks ? acc[km][qt] : f32x16{}, 0, 0, 0);
+          const int qs = (SPG * (2 * ks + qt)) >> 4;
+#pragma unroll
+          for (int u = 0; u < SPG; ++u) {
+            const int e = (SPG * (2 * ks + qt) + u) & 15;
+            const float x = __builtin_amdgcn_exp2f(fmaf(acc[kv][qs][e], c2, -nb[qs]));
+            a[qs][u & 1] = e < 2 ? x : a[qs][u & 1] + x;
+          }
+          // this query tile's sums so far are due here: an empty asm that
+          // takes them in place (ordered against the scheduling barrier;
+          // pure arithmetic alone is not)
+          asm volatile("" : "+v"(a[qs][0]), "+v"(a[qs][1]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        kf0 = kf1;
+        kf1 = kf2;
+      }
+      part[0] = a[0][0] + a[0][1];
+      part[1] = a[1][0] + a[1][1];
+    };
+    // The log2 mass of a block, log2 of its sum, is kept relative to the
+    // running reference m_run of the moment; the last one's (sjb, sev) may
+    // still be in a register.
+    int sjb = 0;
+    float sev = 0.f;
+    // A half whose in-lane sum left [0, 2^13) (a score more than 13 log2
+    // units above the reference, an overflow, or NaN from an infinite
+    // score): the running reference moves to the half's maximum,
+    // rescaling the row's sum so far and `other`, the block's half taken
+    // against the old reference; the half is taken again, and the log masses
+    // of the blocks jdone .. diag already finished move to the new reference
+    // (in fp64, so that they keep their precision however far it moves).
+    auto retake = [&](int kt, int jdone, float (&part)[2], float (&other)[2]) __attribute__((always_inline)) {
+      double dl[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = acc[kt][qt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[kt][qt][e]);
+        const float m_new = fmaxf(m_run[qt], swap32_max(mx));
+        const float f = __builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
+        l_run[qt] *= (double)f;
+        other[qt] *= f;
+        dl[qt] = ((double)m_new - (double)m_run[qt]) * c2d;
+        m_run[qt] = m_new;
+      }
+      const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
+      half_sum(kt, nb, part);
+      const double d = hi ? dl[1] : dl[0];
+      sev = (float)((double)sev - d);
+      // this wave's earlier stores of those rows have landed before they
+      // are read back, and the rewrites before the loop goes on
+      wait_vmcnt<0>();
+      for (int j = jdone; j <= diag; ++j) {
+        float* e = ew + (size_t)j * 64 + lane;
+        *e = (float)((double)*e - d);
+      }
+      wait_vmcnt<0>();
+    };
+    auto escaped = [](const float (&part)[2]) {
+      return __ballot(!(part[0] < 0x1p13f) || !(part[1] < 0x1p13f)) != 0;
+    };
+    // a block's log2 mass relative to m_run from its two halves' sums
+    auto finish = [&](const float (&s0)[2], const float (&s1)[2]) __attribute__((always_inline)) {
+      float evq[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float s = swap32_sum(s0[qt] + s1[qt]);
+        l_run[qt] += (double)s;
+        evq[qt] = __builtin_amdgcn_logf(s);
+      }
+      return hi ? evq[1] : evq[0];
+    };
+
+    // Off the diagonal each block runs in two halves, software-pipelined:
+    // its first half's MFMAs overlap the sums of the previous block's second
+    // half, its second half's MFMAs the sums of its own first half.  Every
+    // iteration stores one log mass (of the block it finished, or again the
+    // last one), so the counted waits see one store per iteration.
+    float p0[2] = {0.f, 0.f}, p1[2] = {0.f, 0.f};
+    bool pend = false;          // block jb + 1 still needs its second half summed
+    static_assert(SNST == 4, "the block loop is unrolled by the ring depth");
+    // one block step; the ring slot is a compile-time constant, so the K
+    // reads take it as an immediate offset
+    auto step = [&](const int t, auto SLOT) __attribute__((always_inline)) {
       switch (min(t, SNST - 1)) {
         case 0: wait_vmcnt<(SNST - 2) * CPW + 0>(); break;
         case 1: wait_vmcnt<(SNST - 2) * CPW + 1>(); break;
@@ -393,109 +577,98 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       __syncthreads();
       issue(t + SNST - 1);
       const int jb = jtop - t;
-      float ev = 0.f;
-      if (jb <= diag) {
-        const char* stage = smem + (t % SNST) * STAGE;
-        f32x16 acc[2][2];
+      constexpr int soff = decltype(SLOT)::value * STAGE;
+      if (jb > diag) {
+        sjb = jb;   // outside the wave's causal range: a slot nothing reads
+        sev = 0.f;
+      } else if (jb == diag) {
+        asm volatile("");  // a real branch: this runs once per row-block
+        mfma_half(soff, 0);
+        mfma_half(soff, 1);
+        // causal mask inside the diagonal block, key index > query index:
+        // tile (kt = 1, qt = 0) lies wholly above the diagonal, (0, 1)
+        // wholly below; in the two diagonal tiles register e holds key
+        // 8 (e / 4) + 4 (L / 32) + e % 4 against query L % 32.  The lane
+        // offset is re-derived here so the 32 predicates are not hoisted
+        // out of the block loop.
+        const int tq = opaque_int(l32 - 4 * hi);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) acc[kt][qt] = f32x16{};
-        // K fragment (kt, ks) of lane L: key 32 kt + L % 32, head-dim slice
-        // 16 ks + 8 (L / 32); read two fragments ahead of the MFMAs using them
-        auto kfrag = [&](int idx) {
-          const int kt = idx & 1, ks = idx >> 1;
-          const int key = 32 * kt + l32;
-          const int chunk = (2 * ks + hi) ^ (key & (CPR - 1));
-          return *reinterpret_cast<const bf16x8*>(stage + key * ROWB + chunk * 16);
-        };
-        bf16x8 kf0 = kfrag(0), kf1 = kfrag(1);
-#pragma unroll
-        for (int idx = 0; idx < 2 * KS; ++idx) {
-          const int kt = idx & 1, ks = idx >> 1;
-          const bf16x8 kf2 = idx + 2 < 2 * KS ? kfrag(idx + 2) : kf0;
-          acc[kt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0][ks], acc[kt][0], 0, 0, 0);
-          acc[kt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[1][ks], acc[kt][1], 0, 0, 0);
-          kf0 = kf1;
-          kf1 = kf2;
+        for (int e = 0; e < 16; ++e) {
+          const bool masked = 8 * (e >> 2) + (e & 3) > tq;
+          acc[0][0][e] = masked ? -INFINITY : acc[0][0][e];
+          acc[1][1][e] = masked ? -INFINITY : acc[1][1][e];
+          acc[1][0][e] = -INFINITY;
         }
-        // per row: its sum over the block relative to the reference m_run,
-        // both 32-key halves (in-lane) and both lane halves (one swap)
-        auto block_sum = [&](int qt, float nb) {
-          float s0 = 0.f, s1 = 0.f;
+        // the diagonal block's maximum is the reference of the row's log2
+        // masses; its sum lies in [1, 64], where the hardware log2 is exact
+        // to an ulp
+        float nb[2];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            s0 += __builtin_amdgcn_exp2f(fmaf(acc[0][qt][e], c2, -nb));
-            s1 += __builtin_amdgcn_exp2f(fmaf(acc[1][qt][e], c2, -nb));
-          }
-          return swap32_sum(s0 + s1);
-        };
-        auto block_max = [&](int qt) {
+        for (int qt = 0; qt < 2; ++qt) {
           float mx = acc[0][qt][0];
 #pragma unroll
           for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[0][qt][e]);
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[1][qt][e]);
-          return swap32_max(mx);
-        };
-        float evq[2];
-        if (jb == diag) {
-          asm volatile("");  // a real branch: this runs once per row-block
-          // causal mask inside the diagonal block, key index > query index:
-          // tile (kt = 1, qt = 0) lies wholly above the diagonal, (0, 1)
-          // wholly below; in the two diagonal tiles register e holds key
-          // 8 (e / 4) + 4 (L / 32) + e % 4 against query L % 32.  The lane
-          // offset is re-derived here so the 32 predicates are not hoisted
-          // out of the block loop.
-          const int t = opaque_int(l32 - 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const bool masked = 8 * (e >> 2) + (e & 3) > t;
-            acc[0][0][e] = masked ? -INFINITY : acc[0][0][e];
-            acc[1][1][e] = masked ? -INFINITY : acc[1][1][e];
-            acc[1][0][e] = -INFINITY;
-          }
-          // the diagonal block's maximum is the reference of the row's
-          // log2 masses; s lies in [1, 64], where the hardware log2 is
-          // exact to an ulp
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            const float mx = block_max(qt);
-            const float s = block_sum(qt, mx * c2);
-            m_ref[qt] = m_run[qt] = mx;
-            eoff[qt] = 0.f;
-            l_run[qt] = (double)s;
-            evq[qt] = __builtin_amdgcn_logf(s);
-          }
-        } else {
-          // Off the diagonal the exponent reference stays m_run; no block
-          // maximum is needed unless a score exceeds it so far that the
-          // sum leaves [0, 2^64) (overflow, or NaN from an infinite score).
-          // Then the wave re-takes the block with its maximum folded in.
-          float s[2];
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) s[qt] = block_sum(qt, m_run[qt] * c2);
-          const bool big = !(s[0] < 0x1p64f) || !(s[1] < 0x1p64f);
-          if (__builtin_expect(__ballot(big) != 0, 0)) {
-            asm volatile("");
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-              const float m_new = fmaxf(m_run[qt], block_max(qt));
-              l_run[qt] *= (double)__builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
-              m_run[qt] = m_new;
-              eoff[qt] = (float)(((double)m_new - (double)m_ref[qt]) * c2d);
-              s[qt] = block_sum(qt, m_new * c2);
-            }
-          }
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            l_run[qt] += (double)s[qt];
-            evq[qt] = __builtin_amdgcn_logf(s[qt]) + eoff[qt];
-          }
+          mx = swap32_max(mx);
+          m_ref[qt] = m_run[qt] = mx;
+          nb[qt] = mx * c2;
         }
-        ev = hi ? evq[1] : evq[0];
+        half_sum(0, nb, p0);
+        half_sum(1, nb, p1);
+        float evq[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float s = swap32_sum(p0[qt] + p1[qt]);
+          l_run[qt] = (double)s;
+          evq[qt] = __builtin_amdgcn_logf(s);
+        }
+        sjb = jb;
+        sev = hi ? evq[1] : evq[0];
+      } else {
+        {
+          // block jb + 1's second half (unused right after the diagonal);
+          // the empty asm keeps its sums here, beside the MFMAs
+          const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
+          pipe_half(soff, 0, 1, nb, p1);
+          asm volatile("" : "+v"(p1[0]), "+v"(p1[1]));
+        }
+        if (pend) {
+          if (__builtin_expect(escaped(p1), 0)) {
+            asm volatile("");
+            retake(1, jb + 2, p1, p0);
+          }
+          sjb = jb + 1;
+          sev = finish(p0, p1);
+        }
+        {
+          const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
+          pipe_half(soff, 1, 0, nb, p0);
+        }
+        if (__builtin_expect(escaped(p0), 0)) {
+          asm volatile("");
+          float none[2] = {0.f, 0.f};
+          retake(0, jb + 1, p0, none);
+        }
+        pend = true;
       }
-      ew[(size_t)jb * 64 + lane] = ev;  // row `lane` of block jb (unused when inactive)
+      ew[(size_t)sjb * 64 + lane] = sev;  // row `lane` of block sjb
+    };
+    for (int t = 0; t <= jtop; t += SNST) {
+      step(t, IC<0>{});
+      if (t + 1 > jtop) break;
+      step(t + 1, IC<1>{});
+      if (t + 2 > jtop) break;
+      step(t + 2, IC<2>{});
+      if (t + 3 > jtop) break;
+      step(t + 3, IC<3>{});
+    }
+    if (pend) {
+      // the second half of the last block, block 0
+      const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
+      half_sum(1, nb, p1);
+      if (escaped(p1)) retake(1, 1, p1, p0);
+      ew[lane] = finish(p0, p1);
     }
 
     wait_vmcnt<0>();
@@ -508,7 +681,10 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       const float mr = hi ? m_ref[1] : m_ref[0];
       const float mu = hi ? m_run[1] : m_run[0];
       const double lr = hi ? l_run[1] : l_run[0];
-      const double lse2 = ((double)mu - (double)mr) * c2d + log2(lr);
+      // the row's log2 normaliser relative to m_run (the reference of every
+      // stored log mass) and to m_ref
+      const double lrun2 = log2(lr);
+      const double lse2 = ((double)mu - (double)mr) * c2d + lrun2;
       const size_t lh = (size_t)l * a.H + h;
       if (lane < ri.rows)
         a.row_lse[lh * a.b.total_q + ri.q0 + lane] = (float)((double)mr * a.scale + lse2 * kLn2);
@@ -524,7 +700,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
           for (int u = 0; u < 8; ++u) e[u] = ew[(size_t)min(j0 + jj + u, ri.ncand - 1) * 64 + lane];
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            if (jj + u < nj) tr[(jj + u) * SEPITCH + lane] = lane < ri.rows ? exp2f((float)((double)e[u] - lse2)) : 0.f;
+            if (jj + u < nj) tr[(jj + u) * SEPITCH + lane] = lane < ri.rows ? exp2f((float)((double)e[u] - lrun2)) : 0.f;
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         if (lane < nj) {

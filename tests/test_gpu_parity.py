@@ -241,6 +241,41 @@ def test_portable_and_mfma_block_stats_agree_with_oracle(B, d):
     assert float((mass_p - mass_f).abs().max()) <= 2e-6
 
 
+@pytest.mark.parametrize("B,d", [(64, 64), (64, 128), (128, 128)])
+def test_block_stats_scores_far_above_the_diagonal_block(B, d):
+    """Keys whose scores lie far above the diagonal block's maximum move the
+    row's exponent reference mid-row: from a first 32-key half, from a second
+    half after the first was summed against the old reference, and where
+    exp2 against the old reference overflows fp32 (block 0).  MFMA and
+    portable kernels against the oracle."""
+    # natural-log logits planted on every row that sees the key, walking down
+    # from the diagonal (64-key blocks): block 4 (about 29 log2 units above
+    # the diagonal's maximum, where an fp32 log mass against the diagonal's
+    # reference would lose the mass's sixth digit), block 3 (first half),
+    # block 2 (second half), block 1 (second half, within the reference's
+    # range), block 0 (first half, exp2 against the old reference overflows)
+    plants = ((4 * 64 + 20, 20.0), (3 * 64 + 8, 75.0), (2 * 64 + 40, 135.0), (64 + 40, 150.0), (10, 250.0))
+
+    def plant(inputs):
+        x = inputs[0]
+        x.q[:, :, 0] = 4.0
+        for pos, logit in plants:
+            x.k[pos, :, 0] = logit * d ** 0.5 / 4.0
+
+    wl = tiny_structured("bf16", workload_id=17, B=B, d=d, H_s=4, H_r=2, num_layers=1,
+                         seqlens=(6 * 64 + 5 if B == 64 else 3 * 128 + 70, 2 * B + 7))
+    masses = []
+    for stages in (("stats",), ()):
+        with mf.force_portable(*stages):
+            run = parity.run_gpu(wl, 0.9, [0], edit=plant)
+        # a score near 250 comes from a d-term fp32 dot product of that size:
+        # its rounding is bounded by d 2^-24 |score|, above the usual 1e-4
+        rep = parity.check_layer(run, 0, lse_tol=parity.LSE_TOL + d * 2.0 ** -24 * 260.0)
+        parity.log(f"[parity] planted scores: mass err {rep.max_mass_err:.2e} lse err {rep.max_lse_err:.2e}")
+        masses.append(run.state.block_mass.clone())
+    assert float((masses[0] - masses[1]).abs().max()) <= 2e-6
+
+
 @pytest.mark.parametrize("B,seqlens", [(64, (64 * 9 + 17, 63, 700)),          # up to 64 candidates per row
                                        (32, (32 * 120 + 5, 40)),              # up to 128
                                        (32, (32 * 250 + 31, 32 * 3))])         # up to 256
