@@ -12,6 +12,8 @@
 //            blocks only (MFMA), P = exp(S * scale - row_lse), and writes
 //            each B x B block key-major (values[e][key][query]) through LDS
 //            so every store is a full 16-byte vector.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -409,16 +411,37 @@ __device__ __forceinline__ void xcopy16(const void* gsrc, char* lds_generic_base
                : "memory", "m0");
 }
 
+// The same copy from a scalar base plus a 32-bit lane offset; m0 is the LDS
+// destination of lane 0.
+__device__ __forceinline__ void xcopy16s(unsigned voff, const void* sbase, unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ unsigned xlds_addr(const char* lds_generic) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_generic);
+}
+// a copy of a lane value the compiler cannot see through
+__device__ __forceinline__ int opaque_int(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+template <int N>
+using IC = std::integral_constant<int, N>;
+
 template <int N>
 __device__ __forceinline__ void xwait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// two floats to bf16 (round to nearest even) in one 32-bit word, lo in the
+// low half: one two-source conversion instruction
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  const unsigned a = __builtin_bit_cast(unsigned short, (bf16)lo);
-  const unsigned b = __builtin_bit_cast(unsigned short, (bf16)hi);
-  return a | (b << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(unsigned, v);
 }
 
 template <int D>
@@ -429,13 +452,9 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
   constexpr int STAGE = 64 * ROWB;
   constexpr int CPW = STAGE / 1024 / 4;
   constexpr int OT = 64 * XPITCH;       // one output tile
-  // the K ring is the only LDS the async copies write; the output tiles and
-  // the block list are separate objects, so their LDS accesses do not have
-  // to wait for copies in flight
+  // the K ring; each output tile goes into the slot whose K its block just
+  // consumed
   extern __shared__ __align__(16) char ring[];
-  // the output tile goes into the K slot just consumed when it fits
-  constexpr bool TILE_IN_RING = STAGE >= OT;
-  __shared__ __align__(16) char otile[TILE_IN_RING ? 16 : OT];
   __shared__ int jlist[kXMaxCb];
   __shared__ int nkept;
 
@@ -506,77 +525,116 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
                                    (size_t)ri.k0 * a.Hkv * D + (size_t)hk * D;
   const size_t kstride = (size_t)a.Hkv * D;
   const int klast = ri.klen - 1;
-  auto issue = [&](int t) {
-    const int j = __builtin_amdgcn_readfirstlane(jlist[t < n ? t : n - 1]);
-    char* stage = ring + (t % XNST) * STAGE;
+  // copy i of this wave: key kkey[i] of the block, source chunk
+  // cc ^ (key % CPR) at byte offset koff[i] from the block's first key row,
+  // whose address is scalar
+  unsigned koff[CPW];
+  int kkey[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int pidx = (i * 4 + w) * 64 + lane;
-      const int key = pidx / CPR, cc = pidx % CPR;
-      const int src_chunk = cc ^ (key & (CPR - 1));
-      const int kabs = min(j * 64 + key, klast);
-      xcopy16(kbase + (size_t)kabs * kstride + src_chunk * 8, stage + (i * 4 + w) * 1024);
+  for (int i = 0; i < CPW; ++i) {
+    const int pidx = (i * 4 + w) * 64 + lane;
+    const int key = pidx / CPR, cc = pidx % CPR;
+    kkey[i] = key;
+    koff[i] = (unsigned)(((size_t)key * kstride + (cc ^ (key & (CPR - 1))) * 8) * 2);
+  }
+  const char* kbytes = reinterpret_cast<const char*>(kbase);
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+    const int j = __builtin_amdgcn_readfirstlane(jlist[t < n ? t : n - 1]);
+    const char* src = kbytes + (size_t)j * 64 * kstride * 2;
+    const unsigned m0 = xlds_addr(ring + slot * STAGE + w * 1024);
+    if (j * 64 + 63 <= klast) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) xcopy16s(koff[i], src, m0 + i * 4 * 1024);
+    } else {
+      // block reaching past the last key: clamp rows to the last key
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int over = max(j * 64 + kkey[i] - klast, 0);
+        xcopy16s(koff[i] - (unsigned)((size_t)over * kstride * 2), src, m0 + i * 4 * 1024);
+      }
     }
   };
-#pragma unroll
-  for (int t = 0; t < XNST - 1; ++t) issue(t);
+  issue(0, 0);
 
   const int diag = ri.ncand - 1;
-  bf16* __restrict__ vals = reinterpret_cast<bf16*>(a.values);
+  const char* __restrict__ vbytes = reinterpret_cast<const char*>(a.values);
+  // per-lane LDS byte addresses, kept opaque so that the compiler holds the
+  // sums rather than re-adding their parts, and every access of a step (its
+  // ring slot known at compile time) is one instruction with an immediate
+  // offset: the K fragment of k-step ks (key 32 kh + L % 32, head-dim slice
+  // 16 ks + 8 (L / 32)), the tile write of row group g, the tile read of
+  // store c
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int key = 32 * kh + l32;
+  const int ring0 = (int)xlds_addr(ring);
+  int kfo[KS], two[4], tro[2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kfo[ks] = opaque_int(ring0 + key * ROWB + (((2 * ks + hi) ^ (key & (CPR - 1))) * 16));
+#pragma unroll
+  for (int g = 0; g < 4; ++g) two[g] = opaque_int(ring0 + xtile_off(key, (32 * qh + 8 * g + 4 * hi) * 2));
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = c * 256 + tid;           // 16-byte chunk: key ch / 8, rows 8 (ch % 8) ..
+    tro[c] = opaque_int(ring0 + xtile_off(ch >> 3, (ch & 7) * 16));
+  }
+  auto lds = [](int addr) { return reinterpret_cast<lds_char*>((uintptr_t)(unsigned)addr); };
 
-  for (int t = 0; t < n; ++t) {
-    switch (min(t, XNST - 1)) {
-      case 0: xwait_vmcnt<(XNST - 2) * CPW + 0>(); break;
-      case 1: xwait_vmcnt<(XNST - 2) * CPW + 2>(); break;
-      default: xwait_vmcnt<(XNST - 2) * CPW + 4>(); break;
-    }
+  // one kept block t in ring slot SLOT: the next block's K goes into the
+  // other slot, the value tile into this one once its K is consumed
+  auto step = [&](const int t, auto SLOT) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    constexpr int soff = slot * STAGE;
+    if (t == 0) xwait_vmcnt<0>();
+    else xwait_vmcnt<2>();   // this slot's copies: only the previous block's two stores are younger
     __syncthreads();
-    issue(t + XNST - 1);
-    const char* stage = ring + (t % XNST) * STAGE;
+    issue(t + 1, slot ^ 1);
     f32x16 acc = f32x16{};
-    const int key = 32 * kh + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int chunk = (2 * ks + hi) ^ (key & (CPR - 1));
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + key * ROWB + chunk * 16);
+      const bf16x8 kf = *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(lds(kfo[ks]) + soff);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc, 0, 0, 0);
     }
+    const bool dg = __builtin_amdgcn_readfirstlane(jlist[t]) == diag;
+    __syncthreads();       // every wave is done reading K from the slot
     // causal mask (diagonal block only) and rows past the row-block: lse2 = inf
-    const bool dg = jlist[t] == diag;
-    char* ot = TILE_IN_RING ? ring + (t % XNST) * STAGE : otile;
-    if (TILE_IN_RING) __syncthreads();       // every wave is done reading K from the slot
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * g + i;
-        const int r = 32 * qh + 8 * g + 4 * hi + i;
-        float x = __builtin_amdgcn_exp2f(fmaf(acc[e], c2, -lse2[e]));
-        if (dg && key > r) x = 0.f;
-        p[i] = x;
+        p[i] = __builtin_amdgcn_exp2f(fmaf(acc[e], c2, -lse2[e]));
       }
-      const int r0 = 32 * qh + 8 * g + 4 * hi;
-      uint2 pk;
-      pk.x = pack_bf16x2(p[0], p[1]);
-      pk.y = pack_bf16x2(p[2], p[3]);
-      *reinterpret_cast<uint2*>(ot + xtile_off(key, r0 * 2)) = pk;
+      if (dg) {
+        asm volatile("");  // a real branch: at most one block per row-block
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key > 32 * qh + 8 * g + 4 * hi + i) p[i] = 0.f;
+      }
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds(two[g]) + soff) = pk;
     }
     __syncthreads();
     // non-temporal stores: the values are read only by a later kernel, and
     // streaming them past L2 keeps the K blocks the row-blocks of this head
     // share resident there
-    bf16* dst = vals + (size_t)(base + t) * 64 * 64;
+    const char* dst = vbytes + (size_t)(base + t) * 64 * 64 * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int ch = c * 256 + tid;           // 16-byte chunk: key ch / 8, rows 8 (ch % 8) ..
-      const int kk = ch >> 3, part = ch & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + xtile_off(kk, part * 16));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * 64 + part * 8));
+      const int ch = c * 256 + tid;
+      const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(lds(tro[c]) + soff);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(const_cast<char*>(dst) + ((ch >> 3) * 64 + (ch & 7) * 8) * 2));
     }
+  };
+  static_assert(XNST == 2 && STAGE >= OT, "two ring slots, each holding an output tile");
+  for (int t = 0; t < n; t += 2) {
+    step(t, IC<0>{});
+    if (t + 1 >= n) break;
+    step(t + 1, IC<1>{});
   }
+  xwait_vmcnt<0>();   // the copy issued past the last block has landed before the LDS is released
 }
-
 
 // 128-row blocks: the same scheme over 64-key halves.  A workgroup walks its
 // row-block's kept 128-key blocks one 64-key half at a time (the K ring holds

@@ -652,7 +652,9 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         }
         pend = true;
       }
-      ew[(size_t)sjb * 64 + lane] = sev;  // row `lane` of block sjb
+      // row `lane` of block sjb; non-temporal: written once, read once by
+      // the epilogue, it should not evict the K blocks other groups re-read
+      __builtin_nontemporal_store(sev, ew + (size_t)sjb * 64 + lane);
     };
     for (int t = 0; t <= jtop; t += SNST) {
       step(t, IC<0>{});
@@ -668,7 +670,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
       half_sum(1, nb, p1);
       if (escaped(p1)) retake(1, 1, p1, p0);
-      ew[lane] = finish(p0, p1);
+      __builtin_nontemporal_store(finish(p0, p1), ew + lane);
     }
 
     wait_vmcnt<0>();
@@ -693,13 +695,14 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
       for (int j0 = 0; j0 < ri.ncand; j0 += 64) {
         const int nj = min(64, ri.ncand - j0);
         // the scratch rows were written by this wave on this CU and its
-        // stores have completed: plain loads see them.  Eight in flight.
-        for (int jj = 0; jj < nj; jj += 8) {
-          float e[8];
+        // stores have completed: plain loads see them.  32 in flight (the
+        // loop's registers are free now): the read-back is latency-bound.
+        for (int jj = 0; jj < nj; jj += 32) {
+          float e[32];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) e[u] = ew[(size_t)min(j0 + jj + u, ri.ncand - 1) * 64 + lane];
+          for (int u = 0; u < 32; ++u) e[u] = __builtin_nontemporal_load(ew + (size_t)min(j0 + jj + u, ri.ncand - 1) * 64 + lane);
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < 32; ++u)
             if (jj + u < nj) tr[(jj + u) * SEPITCH + lane] = lane < ri.rows ? exp2f((float)((double)e[u] - lrun2)) : 0.f;
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
