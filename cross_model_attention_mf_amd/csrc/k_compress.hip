@@ -414,7 +414,15 @@ __device__ __forceinline__ void xcopy16(const void* gsrc, char* lds_generic_base
 // The same copy from a scalar base plus a 32-bit lane offset; m0 is the LDS
 // destination of lane 0.
 __device__ __forceinline__ void xcopy16s(unsigned voff, const void* sbase, unsigned m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0)
+  // the base is uniform; pin it in scalar registers (a value the compiler
+  // keeps in vector registers is not moved for an "s" operand by itself)
+  const uint64_t v = (uint64_t)(uintptr_t)sbase;
+  // (readfirstlane returns int: through unsigned, so the low word does not
+  // sign-extend into the high one)
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  const void* sb = reinterpret_cast<const void*>((uintptr_t)((hi << 32) | lo));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sb), "s"(m0)
                : "memory", "m0");
 }
 __device__ __forceinline__ unsigned xlds_addr(const char* lds_generic) {
@@ -546,11 +554,13 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) xcopy16s(koff[i], src, m0 + i * 4 * 1024);
     } else {
-      // block reaching past the last key: clamp rows to the last key
+      // block reaching past the last key: each row's key clamped to the last
+      // key, addressed from the sequence's first key row
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
-        const int over = max(j * 64 + kkey[i] - klast, 0);
-        xcopy16s(koff[i] - (unsigned)((size_t)over * kstride * 2), src, m0 + i * 4 * 1024);
+        const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
+        const int kk = min(j * 64 + kkey[i], klast);
+        xcopy16(kbytes + (size_t)kk * kstride * 2 + chb, ring + slot * STAGE + (i * 4 + w) * 1024);
       }
     }
   };
@@ -727,48 +737,82 @@ __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) 
                                    (size_t)ri.k0 * a.Hkv * D + (size_t)hk * D;
   const size_t kstride = (size_t)a.Hkv * D;
   const int klast = ri.klen - 1;
-  // stage t: key half t % 2 of kept block t / 2
-  auto issue = [&](int t) {
+  // copy i of this wave: key kkey[i] of the stage, byte offset koff[i] from
+  // the stage's first key row (scalar), as in the 64-row kernel
+  unsigned koff[CPW];
+  int kkey[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int pidx = (i * 4 + w) * 64 + lane;
+    const int key = pidx / CPR, cc = pidx % CPR;
+    kkey[i] = key;
+    koff[i] = (unsigned)(((size_t)key * kstride + (cc ^ (key & (CPR - 1))) * 8) * 2);
+  }
+  const char* kbytes = reinterpret_cast<const char*>(kbase);
+  // stage t: key half t % 2 of kept block t / 2, into ring slot t % 2
+  auto issue = [&](int t) __attribute__((always_inline)) {
     const int tt = t < 2 * n ? t : 2 * n - 1;
     const int j = __builtin_amdgcn_readfirstlane(jlist[tt >> 1]);
-    char* stage = ring + (t % XNST) * STAGE;
+    const int k0 = j * BB + 64 * (tt & 1);
+    const char* src = kbytes + (size_t)k0 * kstride * 2;
+    const unsigned m0 = xlds_addr(ring + (t % XNST) * STAGE + w * 1024);
+    if (k0 + 63 <= klast) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int pidx = (i * 4 + w) * 64 + lane;
-      const int key = pidx / CPR, cc = pidx % CPR;
-      const int src_chunk = cc ^ (key & (CPR - 1));
-      const int kabs = min(j * BB + 64 * (tt & 1) + key, klast);
-      xcopy16(kbase + (size_t)kabs * kstride + src_chunk * 8, stage + (i * 4 + w) * 1024);
+      for (int i = 0; i < CPW; ++i) xcopy16s(koff[i], src, m0 + i * 4 * 1024);
+    } else {
+      // rows past the last key (the second half may start past it): each
+      // row's key clamped to the last key, addressed from the sequence's
+      // first key row
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
+        const int kk = min(k0 + kkey[i], klast);
+        xcopy16(kbytes + (size_t)kk * kstride * 2 + chb, ring + (t % XNST) * STAGE + (i * 4 + w) * 1024);
+      }
     }
   };
-#pragma unroll
-  for (int t = 0; t < XNST - 1; ++t) issue(t);
+  issue(0);
 
   const int diag = ri.ncand - 1;
-  bf16* __restrict__ vals = reinterpret_cast<bf16*>(a.values);
+  const char* __restrict__ vbytes = reinterpret_cast<const char*>(a.values);
+  // per-lane LDS byte addresses (opaque, as in the 64-row kernel): K
+  // fragment ks of key 32 kh + L % 32 in slot 0, the tile write of (half
+  // hf, row group g), the tile read of store c
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int key = 32 * kh + l32;
+  const int ring0 = (int)xlds_addr(ring), tile0 = (int)xlds_addr(otile);
+  int kfo[KS], two[2][4], tro[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kfo[ks] = opaque_int(ring0 + key * ROWB + (((2 * ks + hi) ^ (key & (CPR - 1))) * 16));
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) two[hf][g] = opaque_int(tile0 + xtile2_off(key, (64 * hf + 32 * qh + 8 * g + 4 * hi) * 2));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = c * 256 + tid;          // 16-byte chunk: key ch / 16, rows 8 (ch % 16) ..
+    tro[c] = opaque_int(tile0 + xtile2_off(ch >> 4, (ch & 15) * 16));
+  }
+  auto lds = [](int addr) { return reinterpret_cast<lds_char*>((uintptr_t)(unsigned)addr); };
 
-  for (int t = 0; t < 2 * n; ++t) {
-    switch (min(t, XNST - 1)) {
-      case 0: xwait_vmcnt<(XNST - 2) * CPW + 0>(); break;
-      case 1: xwait_vmcnt<(XNST - 2) * CPW + 2>(); break;
-      default: xwait_vmcnt<(XNST - 2) * CPW + 4>(); break;
-    }
+  // stage t (key half KB = t % 2, the ring slot too) of kept block t / 2
+  auto step = [&](const int t, auto KBC) __attribute__((always_inline)) {
+    constexpr int kb = decltype(KBC)::value;
+    constexpr int soff = kb * STAGE;
+    if (t == 0) xwait_vmcnt<0>();
+    else xwait_vmcnt<4>();   // this slot's copies: only the previous stage's four stores are younger
     __syncthreads();
-    issue(t + XNST - 1);
-    const char* stage = ring + (t % XNST) * STAGE;
-    const int kb = t & 1;                    // key half of the block
+    issue(t + 1);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
-    const int key = 32 * kh + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int chunk = (2 * ks + hi) ^ (key & (CPR - 1));
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + key * ROWB + chunk * 16);
+      const bf16x8 kf = *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(lds(kfo[ks]) + soff);
       acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][ks], kf, acc[0], 0, 0, 0);
       acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][ks], kf, acc[1], 0, 0, 0);
     }
     // causal mask (diagonal block only: key 64 kb + key against row 64 a + r)
     // and rows past the row-block (lse2 = inf)
-    const bool dg = jlist[t >> 1] == diag;
+    const bool dg = __builtin_amdgcn_readfirstlane(jlist[t >> 1]) == diag;
     const int kr = 64 * kb + key;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -778,28 +822,34 @@ __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g + i;
-          const int r = 64 * hf + 32 * qh + 8 * g + 4 * hi + i;
-          float x = __builtin_amdgcn_exp2f(fmaf(acc[hf][e], c2, -lse2[hf][e]));
-          if (dg && kr > r) x = 0.f;
-          p[i] = x;
+          p[i] = __builtin_amdgcn_exp2f(fmaf(acc[hf][e], c2, -lse2[hf][e]));
         }
-        const int r0 = 64 * hf + 32 * qh + 8 * g + 4 * hi;
-        uint2 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
-        *reinterpret_cast<uint2*>(otile + xtile2_off(key, r0 * 2)) = pk;
+        if (dg) {
+          asm volatile("");  // a real branch: at most one block per row-block
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kr > 64 * hf + 32 * qh + 8 * g + 4 * hi + i) p[i] = 0.f;
+        }
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds(two[hf][g])) = pk;
       }
     __syncthreads();
     // 64 key rows of 256 bytes: key 64 kb + kk of value block t / 2
-    bf16* dst = vals + (size_t)(base + (t >> 1)) * BB * BB + (size_t)(64 * kb) * BB;
+    const char* dst = vbytes + ((size_t)(base + (t >> 1)) * BB * BB + (size_t)(64 * kb) * BB) * 2;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int ch = c * 256 + tid;          // 16-byte chunk: key ch / 16, rows 8 (ch % 16) ..
-      const int kk = ch >> 4, part = ch & 15;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(otile + xtile2_off(kk, part * 16));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + kk * BB + part * 8));
+      const int ch = c * 256 + tid;
+      const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(lds(tro[c]));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(const_cast<char*>(dst) + ((ch >> 4) * BB + (ch & 15) * 8) * 2));
     }
+  };
+  static_assert(XNST == 2, "two ring slots, one per key half");
+  for (int t = 0; t < 2 * n; t += 2) {
+    step(t, IC<0>{});
+    step(t + 1, IC<1>{});
   }
+  xwait_vmcnt<0>();   // the copy issued past the last stage has landed before the LDS is released
 }
 
 template <typename T, int B, int D>

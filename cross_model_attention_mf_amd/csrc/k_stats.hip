@@ -231,7 +231,15 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, char* lds_generi
 // counted waits and barriers do); one wait state between the M0 write and
 // the copy reading it.
 __device__ __forceinline__ void copy16_saddr(unsigned voff, const void* sbase, unsigned m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0)
+  // the base is uniform; pin it in scalar registers (a value the compiler
+  // keeps in vector registers is not moved for an "s" operand by itself)
+  const uint64_t v = (uint64_t)(uintptr_t)sbase;
+  // (readfirstlane returns int: through unsigned, so the low word does not
+  // sign-extend into the high one)
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  const void* sb = reinterpret_cast<const void*>((uintptr_t)((hi << 32) | lo));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sb), "s"(m0)
                : "memory", "m0");
 }
 
@@ -389,11 +397,13 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
 #pragma unroll
         for (int i = 0; i < CPW; ++i) copy16_saddr(koff[i], src, m0 + i * SQ * 1024);
       } else {
-        // block reaching past the last key: clamp rows to the last key
+        // block reaching past the last key: each row's key clamped to the
+        // last key, addressed from the sequence's first key row
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-          const int over = max(jb * 64 + kkey[i] - klast, 0);
-          copy16_saddr(koff[i] - (unsigned)((size_t)over * kstride * 2), src, m0 + i * SQ * 1024);
+          const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
+          const int kk = min(jb * 64 + kkey[i], klast);
+          copy16_to_lds(kbytes + (size_t)kk * kstride * 2 + chb, smem + (t % SNST) * STAGE + (i * SQ + w) * 1024);
         }
       }
     };
