@@ -397,6 +397,9 @@ __device__ __forceinline__ int xtile_off(int key, int byte) {   // byte < 128
   return key * XPITCH + ((((byte >> 4) ^ ((key >> 1) & 7))) << 4) + (byte & 15);
 }
 constexpr int kXMaxCb = (MF_MAX_KEYS + 63) / 64;   // column blocks of the longest sequence
+// K rows of one sequence are addressed by 32-bit byte offsets from its first
+// key row (at most MF_MAX_KEYS keys of at most 64 heads x 128 dims, bf16)
+static_assert((unsigned long long)MF_MAX_KEYS * 64 * 128 * 2 < (1ull << 32), "32-bit K row offsets");
 
 // Async 16-byte-per-lane copy HBM -> LDS (lane L lands at base + 16 L).
 // Issued as inline assembly so the compiler does not track it: it would
@@ -560,7 +563,8 @@ __global__ void __launch_bounds__(256, 4) extract_mfma_kernel(ExtractArgs a) {
       for (int i = 0; i < CPW; ++i) {
         const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
         const int kk = min(j * 64 + kkey[i], klast);
-        xcopy16(kbytes + (size_t)kk * kstride * 2 + chb, ring + slot * STAGE + (i * 4 + w) * 1024);
+        // below 2^32: a sequence has at most MF_MAX_KEYS keys of at most 64 heads x 128 dims
+        xcopy16s((unsigned)((size_t)kk * kstride * 2) + chb, kbytes, m0 + i * 4 * 1024);
       }
     }
   };
@@ -767,7 +771,8 @@ __global__ void __launch_bounds__(256, 2) extract_mfma128_kernel(ExtractArgs a) 
       for (int i = 0; i < CPW; ++i) {
         const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
         const int kk = min(k0 + kkey[i], klast);
-        xcopy16(kbytes + (size_t)kk * kstride * 2 + chb, ring + (t % XNST) * STAGE + (i * 4 + w) * 1024);
+        // below 2^32: a sequence has at most MF_MAX_KEYS keys of at most 64 heads x 128 dims
+        xcopy16s((unsigned)((size_t)kk * kstride * 2) + chb, kbytes, m0 + i * 4 * 1024);
       }
     }
   };

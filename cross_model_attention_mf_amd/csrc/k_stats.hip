@@ -217,6 +217,9 @@ int launch_d(const StatsArgs& a, void* stream) {
 // head stays in one XCD's L2.
 // ---------------------------------------------------------------------------
 constexpr int SQ = 4;        // row-blocks (waves) per workgroup
+// K rows of one sequence are addressed by 32-bit byte offsets from its first
+// key row (at most MF_MAX_KEYS keys of at most 64 heads x 128 dims, bf16)
+static_assert((unsigned long long)MF_MAX_KEYS * 64 * 128 * 2 < (1ull << 32), "32-bit K row offsets");
 constexpr int SNST = 4;      // K ring depth
 constexpr int SEPITCH = 65;  // floats per row of an epilogue transpose
 
@@ -398,12 +401,13 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         for (int i = 0; i < CPW; ++i) copy16_saddr(koff[i], src, m0 + i * SQ * 1024);
       } else {
         // block reaching past the last key: each row's key clamped to the
-        // last key, addressed from the sequence's first key row
+        // last key, addressed from the sequence's first key row (scalar)
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
           const unsigned chb = koff[i] - (unsigned)((size_t)kkey[i] * kstride * 2);   // the chunk's byte offset in its row
           const int kk = min(jb * 64 + kkey[i], klast);
-          copy16_to_lds(kbytes + (size_t)kk * kstride * 2 + chb, smem + (t % SNST) * STAGE + (i * SQ + w) * 1024);
+          // below 2^32: a sequence has at most MF_MAX_KEYS keys of at most 64 heads x 128 dims
+          copy16_saddr((unsigned)((size_t)kk * kstride * 2) + chb, kbytes, m0 + i * SQ * 1024);
         }
       }
     };
@@ -485,30 +489,40 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
     auto pipe_half = [&](int soff, int km, int kv, const float (&nb)[2], float (&part)[2]) __attribute__((always_inline)) {
       constexpr int SPG = 16 / KS;   // scores summed per MFMA
       static_assert(SPG * KS == 16 && SPG % 2 == 0, "two sum chains per query tile");
-      // K fragments read two k-steps ahead of the MFMAs using them
-      bf16x8 kf0 = kfrag(soff, km, 0), kf1 = kfrag(soff, km, 1);
+      constexpr int KA = 2;          // K fragments read this many k-steps ahead of their MFMAs
+      constexpr bool GROUP_KS = false;   // one scheduling group per k-step (two MFMAs), else per MFMA
+      // a shift register of K fragments: kw[0] feeds this k-step's MFMAs
+      bf16x8 kw[KA + 1];
+#pragma unroll
+      for (int i = 0; i < KA; ++i) kw[i] = kfrag(soff, km, i < KS ? i : 0);
       float a[2][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf2 = ks + 2 < KS ? kfrag(soff, km, ks + 2) : kf0;
+        kw[KA] = ks + KA < KS ? kfrag(soff, km, ks + KA) : kw[0];
+        const int qs = (SPG * 2 * ks) >> 4;   // the query tile this k-step's sums belong to
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          acc[km][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[qt][ks], ks ? acc[km][qt] : f32x16{}, 0, 0, 0);
-          const int qs = (SPG * (2 * ks + qt)) >> 4;
+          acc[km][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw[0], qf[qt][ks], ks ? acc[km][qt] : f32x16{}, 0, 0, 0);
 #pragma unroll
           for (int u = 0; u < SPG; ++u) {
             const int e = (SPG * (2 * ks + qt) + u) & 15;
             const float x = __builtin_amdgcn_exp2f(fmaf(acc[kv][qs][e], c2, -nb[qs]));
             a[qs][u & 1] = e < 2 ? x : a[qs][u & 1] + x;
           }
-          // this query tile's sums so far are due here: an empty asm that
-          // takes them in place (ordered against the scheduling barrier;
-          // pure arithmetic alone is not)
+          if (!GROUP_KS) {
+            // this query tile's sums so far are due here: an empty asm that
+            // takes them in place (ordered against the scheduling barrier;
+            // pure arithmetic alone is not)
+            asm volatile("" : "+v"(a[qs][0]), "+v"(a[qs][1]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (GROUP_KS) {
           asm volatile("" : "+v"(a[qs][0]), "+v"(a[qs][1]));
           __builtin_amdgcn_sched_barrier(0);
         }
-        kf0 = kf1;
-        kf1 = kf2;
+#pragma unroll
+        for (int i = 0; i < KA; ++i) kw[i] = kw[i + 1];
       }
       part[0] = a[0][0] + a[0][1];
       part[1] = a[1][0] + a[1][1];
