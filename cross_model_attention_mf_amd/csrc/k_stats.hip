@@ -481,49 +481,58 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         part[qt] = a0 + a1;
       }
     };
-    // The MFMAs of half km of the block in `stage` on the matrix pipe while
-    // the vector pipe sums half kv of the scores already in acc: each MFMA is
-    // issued with the fma, exp2 and add of 16 / KS of those scores, and a
-    // scheduling barrier after each such group keeps that order.  The sums
-    // run in half_sum's order, so both give the same bits.
-    auto pipe_half = [&](int soff, int km, int kv, const float (&nb)[2], float (&part)[2]) __attribute__((always_inline)) {
-      constexpr int SPG = 16 / KS;   // scores summed per MFMA
+    // The MFMAs of half km of the block at ring offset soff on the matrix
+    // pipe while the vector pipe sums half kv of the scores already in acc.
+    // The work runs in 2 KS scheduling groups plus LEAD: group g issues MFMA
+    // g - LEAD (k-step (g - LEAD) / 2, query tile (g - LEAD) % 2) and the
+    // fma, exp2 and add of the g-th 16 / KS of the other half's scores, so
+    // the vector work leads by LEAD groups and covers the first K reads.  A
+    // scheduling barrier after each group keeps that order.  K fragments are
+    // read KA k-steps ahead through a shift register that starts from kin;
+    // with NEXT the last k-steps read the first KA fragments of half 1 into
+    // kout.  The sums run in half_sum's order, so both give the same bits.
+    constexpr int KA = 2;     // K fragments read this many k-steps ahead of their MFMAs
+    constexpr int LEAD = 1;   // groups the vector work leads the matrix work by
+    auto pipe_half = [&](int soff, int km, int kv, const float (&nb)[2], float (&part)[2], const bf16x8 (&kin)[KA],
+                         bf16x8 (&kout)[KA], auto NEXT) __attribute__((always_inline)) {
+      constexpr bool next = decltype(NEXT)::value != 0;
+      constexpr int SPG = 16 / KS;   // scores summed per group
+      constexpr int NM = 2 * KS;     // MFMAs of the half
       static_assert(SPG * KS == 16 && SPG % 2 == 0, "two sum chains per query tile");
-      constexpr int KA = 2;          // K fragments read this many k-steps ahead of their MFMAs
-      constexpr bool GROUP_KS = false;   // one scheduling group per k-step (two MFMAs), else per MFMA
-      // a shift register of K fragments: kw[0] feeds this k-step's MFMAs
       bf16x8 kw[KA + 1];
 #pragma unroll
-      for (int i = 0; i < KA; ++i) kw[i] = kfrag(soff, km, i < KS ? i : 0);
+      for (int i = 0; i < KA; ++i) kw[i] = kin[i];
       float a[2][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kw[KA] = ks + KA < KS ? kfrag(soff, km, ks + KA) : kw[0];
-        const int qs = (SPG * 2 * ks) >> 4;   // the query tile this k-step's sums belong to
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+      for (int g = 0; g < NM + LEAD; ++g) {
+        const int m = g - LEAD;
+        if (m >= 0 && m < NM) {
+          const int ks = m >> 1, qt = m & 1;
+          if (qt == 0)
+            kw[KA] = ks + KA < KS ? kfrag(soff, km, ks + KA) : (next ? kfrag(soff, 1, ks + KA - KS) : kw[0]);
           acc[km][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw[0], qf[qt][ks], ks ? acc[km][qt] : f32x16{}, 0, 0, 0);
+          if (qt == 1) {
+#pragma unroll
+            for (int i = 0; i < KA; ++i) kw[i] = kw[i + 1];
+          }
+        }
+        if (g < NM) {
+          const int qs = (SPG * g) >> 4;   // the query tile of this group's scores
 #pragma unroll
           for (int u = 0; u < SPG; ++u) {
-            const int e = (SPG * (2 * ks + qt) + u) & 15;
+            const int e = (SPG * g + u) & 15;
             const float x = __builtin_amdgcn_exp2f(fmaf(acc[kv][qs][e], c2, -nb[qs]));
             a[qs][u & 1] = e < 2 ? x : a[qs][u & 1] + x;
           }
-          if (!GROUP_KS) {
-            // this query tile's sums so far are due here: an empty asm that
-            // takes them in place (ordered against the scheduling barrier;
-            // pure arithmetic alone is not)
-            asm volatile("" : "+v"(a[qs][0]), "+v"(a[qs][1]));
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        if (GROUP_KS) {
+          // this query tile's sums so far are due here: an empty asm that
+          // takes them in place (ordered against the scheduling barrier;
+          // pure arithmetic alone is not)
           asm volatile("" : "+v"(a[qs][0]), "+v"(a[qs][1]));
-          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < KA; ++i) kw[i] = kw[i + 1];
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < KA; ++i) kout[i] = kw[i];
       part[0] = a[0][0] + a[0][1];
       part[1] = a[1][0] + a[1][1];
     };
@@ -650,11 +659,14 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         sjb = jb;
         sev = hi ? evq[1] : evq[0];
       } else {
+        bf16x8 kh0[KA], kh1[KA];   // first K fragments of the block's halves 0 and 1
+#pragma unroll
+        for (int i = 0; i < KA; ++i) kh0[i] = kfrag(soff, 0, i);
         {
           // block jb + 1's second half (unused right after the diagonal);
           // the empty asm keeps its sums here, beside the MFMAs
           const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
-          pipe_half(soff, 0, 1, nb, p1);
+          pipe_half(soff, 0, 1, nb, p1, kh0, kh1, IC<1>{});
           asm volatile("" : "+v"(p1[0]), "+v"(p1[1]));
         }
         if (pend) {
@@ -667,7 +679,7 @@ stats_mfma_kernel(StatsArgs a, int32_t* hdr, const int32_t* __restrict__ table, 
         }
         {
           const float nb[2] = {m_run[0] * c2, m_run[1] * c2};
-          pipe_half(soff, 1, 0, nb, p0);
+          pipe_half(soff, 1, 0, nb, p0, kh1, kh0, IC<0>{});
         }
         if (__builtin_expect(escaped(p0), 0)) {
           asm volatile("");
