@@ -472,11 +472,12 @@ def pipelined_bench(reps: int, tau: float, layers: int, groups: int):
                       "results": res})
 
 
-def measure_path(wl, tau: float, steps: int, warmup: int, workload_name: str):
+def measure_path(wl, tau: float, steps: int, warmup: int, workload_name: str, split: bool = False):
     """Time `steps` whole-path steps (statistics, compression, fused step,
     each bracketed by HIP events on the launch stream) of workload `wl` at
-    threshold tau, inputs resident in HBM.  Returns the bench record and the
-    sender state."""
+    threshold tau, inputs resident in HBM.  split: the fused step through
+    mf_mapped_attn_v_split (its workspace allocated before the timed steps).
+    Returns the bench record and the sender state."""
     import torch
 
     from cross_model_attention_mf_amd import mapflow as mf
@@ -498,6 +499,7 @@ def measure_path(wl, tau: float, steps: int, warmup: int, workload_name: str):
     lmap = list(range(L))
     desc_r = mf.receiver_desc(v, wl.H_s, wl.H_r, wl.d, wl.B, lmap, L, out[0].numel(), st.col_idx.numel())
     stream = torch.cuda.current_stream()
+    split_ws = pipeline.split_workspace(desc_r, batch, dev) if split else None
     print(f"[bench] nnz={cap} blocks ({cap * wl.B * wl.B * 2 / 1e9:.2f} GB of values)", file=sys.stderr, flush=True)
 
     def step(ev=None):
@@ -510,7 +512,10 @@ def measure_path(wl, tau: float, steps: int, warmup: int, workload_name: str):
                            st.col_idx, st.values, cap, st.workspace, sync_count=False)
         if ev is not None:
             ev[2].record(stream)
-        mf.mapped_attn_v(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out)
+        if split:
+            mf.mapped_attn_v_split(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out, split_ws)
+        else:
+            mf.mapped_attn_v(desc_r, batch, st.row_ptr, st.col_idx, st.values, W, v, out)
         if ev is not None:
             ev[3].record(stream)
 
@@ -625,7 +630,10 @@ def sweep_bench(steps: int, warmup: int):
                   "bf16 causal 4096 tokens, one mapped layer, sender 32 heads -> receiver 24 heads, d=128, B=64, "
                   "structured Q/K"))
     for tag, wl, tau, name in cases:
-        res, st, batch, cap, _ = measure_path(wl, tau, steps, warmup, name)
+        # the split entry point: the 4K layer's longest unions are cut into
+        # column ranges; the 8K launches fill the chip and take no splits
+        res, st, batch, cap, _ = measure_path(wl, tau, steps, warmup, name, split=True)
+        res["mapped_entry"] = "mf_mapped_attn_v_split"
         res.update(union_stats(st, batch, cap, wl))
         tgt = K3_TARGET_US[(tag, tau)]
         res["metric"] = f"headline sweep: {tag} step at tau {tau}"

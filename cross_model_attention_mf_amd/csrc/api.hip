@@ -404,6 +404,34 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch, 
   return e ? hip_fail(e, fn) : MF_OK;
 }
 
+size_t mf_mapped_split_workspace_size(const mf_receiver_desc* desc, const mf_batch* batch) {
+  mf::clear_error();
+  if (!desc || !batch || desc->num_layers < 0 || desc->num_layers > MF_MAX_LAYERS || (desc->num_layers > 0 && !desc->layer_map))
+    return 0;
+  const mf::MappedArgs a = mapped_args(desc, batch, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return mf::mapped_split_workspace_bytes(a, mf::mapped_splits(a, desc->dtype, allow_fast_mapped(), device_lds_limit()));
+}
+
+mf_status mf_mapped_attn_v_split(const mf_receiver_desc* desc, const mf_batch* batch, const int32_t* row_ptr,
+                                 const int32_t* col_idx, const void* values, const float* W, const void* v, void* o,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  mf::clear_error();
+  const char* fn = "mf_mapped_attn_v_split";
+  bool empty = false;
+  mf_status st = check_receiver(desc, batch, row_ptr, col_idx, values, W, v, o, fn, &empty);
+  if (st || empty) return st;
+  const mf::MappedArgs a = mapped_args(desc, batch, row_ptr, col_idx, values, W, v, o);
+  const size_t need = mf::mapped_split_workspace_bytes(a, mf::mapped_splits(a, desc->dtype, allow_fast_mapped(),
+                                                                            device_lds_limit()));
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MF_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace ? workspace_bytes : (size_t)0,
+                need);
+  if (need > 0 && ((uintptr_t)workspace & 255u))
+    return fail(MF_ERR_INVALID, "%s: workspace not 256-byte aligned", fn);
+  const int e = mf::launch_mapped_split(a, desc->dtype, workspace, stream, allow_fast_mapped(), device_lds_limit());
+  return e ? hip_fail(e, fn) : MF_OK;
+}
+
 mf_status mf_mapped_attn_v_multi(const mf_receiver_desc* const* descs, int n_receivers, const mf_batch* batch,
                                  const int32_t* row_ptr, const int32_t* col_idx, const void* values,
                                  const float* const* W, const void* const* v, void* const* o, void* stream) {

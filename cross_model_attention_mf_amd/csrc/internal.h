@@ -107,6 +107,12 @@ struct MappedArgs {
   // every receiver of the launch (the MFMA kernel reads these)
   int32_t nrecv;
   MappedRecv rx[MF_MAX_RECEIVERS];
+  // union splits (MFMA kernel, one receiver): up to nsplit workgroups share a
+  // unit's union walk, each over a column range, and write fp32 partial
+  // outputs that a second kernel sums; 0 or 1: no splits
+  int32_t nsplit;
+  float* partial;           // [unit x group][nsplit][64 rows][8 heads][d]
+  int32_t* split_count;     // [unit x group]: the splits a unit took
 };
 
 // Least-squares fit of the head mix: the two CSRs, the layer pairing and
@@ -139,6 +145,12 @@ int launch_select(const SelectArgs& a, void* stream);
 int launch_scan(const ScanArgs& a, void* stream);
 int launch_extract(const ExtractArgs& a, mf_dtype dt, void* stream);
 int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);
+// the union-split launch of one receiver: the splits it would use (1: none)
+// and the workspace they need, and the launch itself (the plain launch when
+// no split applies)
+int mapped_splits(const MappedArgs& a, mf_dtype dt, bool allow_fast, size_t lds_limit);
+size_t mapped_split_workspace_bytes(const MappedArgs& a, int nsplit);
+int launch_mapped_split(MappedArgs a, mf_dtype dt, void* ws, void* stream, bool allow_fast, size_t lds_limit);
 // several receivers on one CSR: one launch when the MFMA kernel covers them
 // all, else one launch per receiver
 int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit);

@@ -255,6 +255,7 @@ struct alignas(16) UnionInfo {
 };
 
 constexpr int kUnionSlots = 3;
+constexpr int kSplitBlocks = 4;   // kept blocks of a unit's longest head per union split
 constexpr size_t kMapMeta = kUnionSlots * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
 constexpr int kMapWaves = 8;
 constexpr int kMapRows = 64;   // query rows per workgroup
@@ -361,17 +362,25 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
   // kept values.  Units are dealt to the XCDs in turn, latest row-blocks
   // first: a row-block's union (and work) grows with its causal range, and
   // the short ones then fill the tail.
+  // With union splits, the nsplit workgroups of a unit's head group each
+  // walk one column range of its union (split sp), the ranges of one split
+  // index following each other group by group.
   const int nitems = a.b.total_rb * C::QH;
-  int item, grp, l;
+  const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
+  int item, grp, l, sp;
   {
     const long long nu = (long long)nitems * a.L;
     const long long pos = blockIdx.x / kXcds;
-    const long long u = (long long)(blockIdx.x % kXcds) + (long long)kXcds * (pos / ngroups);
+    const long long per = (long long)ngroups * nsplit;
+    const long long u = (long long)(blockIdx.x % kXcds) + (long long)kXcds * (pos / per);
     if (u >= nu) return;
-    grp = (int)(pos % ngroups);
+    grp = (int)(pos % per % ngroups);
+    sp = (int)(pos % per / ngroups);
     item = nitems - 1 - (int)(u / a.L);
     l = (int)(u % a.L);
   }
+  // the unit's head group in the split bookkeeping
+  const long long ug = ((long long)item * a.L + l) * ngroups + grp;
   // the receiver this group belongs to, and the group's index in it
   int rk = 0;
   for (int k = 1; k < a.nrecv; ++k) rk = grp >= a.rx[k].group0 ? k : rk;
@@ -402,8 +411,35 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       const size_t row = ((size_t)sl * a.Hs + lane) * a.b.total_rb + rb;
       mptr = min((int64_t)a.row_ptr[row], a.csr_capacity);
       mend = min((int64_t)a.row_ptr[row + 1], a.csr_capacity);
-      if (mptr < mend) c0 = a.col_idx[mptr];
     }
+    if (nsplit > 1) {
+      // splits this unit takes: about kSplitBlocks kept blocks of its longest
+      // head per split, at most one per causal column block; split sp walks
+      // columns [sp ncand / su, (sp + 1) ncand / su) of every head's list,
+      // whose ends a binary search finds
+      int mx = lane < a.Hs ? (int)(mend - mptr) : 0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+      const int su = max(1, min(min(nsplit, ri.ncand), (mx + kSplitBlocks - 1) / kSplitBlocks));
+      if (lane == 0) UI[0].pad = su;
+      if (sp < su && lane < a.Hs) {
+        const int clo = (int)((long long)sp * ri.ncand / su), chi = (int)((long long)(sp + 1) * ri.ncand / su);
+        int64_t lo0 = mptr, hi0 = mend, lo1 = mptr, hi1 = mend;   // first entry >= clo, >= chi
+        while (lo0 < hi0 || lo1 < hi1) {
+          if (lo0 < hi0) {
+            const int64_t m = (lo0 + hi0) >> 1;
+            if (a.col_idx[m] < clo) lo0 = m + 1; else hi0 = m;
+          }
+          if (lo1 < hi1) {
+            const int64_t m = (lo1 + hi1) >> 1;
+            if (a.col_idx[m] < chi) lo1 = m + 1; else hi1 = m;
+          }
+        }
+        mptr = lo0;
+        mend = lo1;
+      }
+    }
+    if (mptr < mend) c0 = a.col_idx[mptr];
     curcol[lane] = c0;
   }
   // wave 0: next block of the union and the heads that keep it; the heads'
@@ -438,6 +474,9 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     for (int c = 0; c < C::MC; ++c) async_copy4(&kNoColumn, smem + C::DOFF);
   };
   __syncthreads();
+  // splits past the ones this unit takes have nothing to do
+  const int su = nsplit > 1 ? __builtin_amdgcn_readfirstlane(UI[0].pad) : 1;
+  if (sp >= su) return;
   if (wave == 0) merge(&UI[0]);
   wait_vmcnt<0>();
   __syncthreads();
@@ -778,6 +817,22 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 
   // ---- output: stage [q][8 heads][d] in LDS, then 16-byte stores of whole rows
   wait_vmcnt<0>();
+  if (nsplit > 1 && sp == 0 && tid == 0) a.split_count[ug] = su;
+  if (su > 1) {
+    // a split's fp32 partial, [q][8 heads][d], straight from the registers
+    // (lanes 0-31 and 32-63 each write 128 contiguous bytes of a row)
+    float* __restrict__ pd = a.partial + ((size_t)ug * nsplit + sp) * (size_t)(kMapRows * 8 * D);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qq = 32 * qt + 8 * (i >> 2) + 4 * lh + (i & 3);
+          pd[((size_t)qq * 8 + wave) * D + 32 * nt + (lane & 31)] = O[qt][nt][i];
+        }
+    return;
+  }
   __syncthreads();
   bf16* stage = reinterpret_cast<bf16*>(smem);
 #pragma unroll
@@ -832,7 +887,7 @@ int launch_fast_cfg(const MappedArgs& a, void* stream) {
   int ngroups = 0;
   for (int k = 0; k < a.nrecv; ++k) ngroups += (a.rx[k].Hr + 7) / 8;
   const long long nu = (long long)a.b.total_rb * C::QH * a.L;
-  const long long per_xcd = (nu + kXcds - 1) / kXcds * ngroups;
+  const long long per_xcd = (nu + kXcds - 1) / kXcds * ngroups * (a.nsplit > 1 ? a.nsplit : 1);
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(kMapWaves * 64), C::LDS, (hipStream_t)stream,
                      a, ngroups);
   return (int)hipGetLastError();
@@ -895,6 +950,42 @@ int launch_gd(const MappedArgs& a, void* stream) {
   return (int)hipErrorInvalidValue;
 }
 
+// Sum of a unit's split partials (in split order, so repeated calls give the
+// same bits) into its bf16 output rows.  Workgroup (unit head group ug, row
+// slice z) covers 8 query rows x 8 receiver heads x d; units that took one
+// split wrote their output themselves.
+template <int D>
+__global__ void __launch_bounds__(256) mapped_split_reduce_kernel(MappedArgs a, int ngroups, int qh) {
+  const long long ug = blockIdx.x / 8;
+  const int z = blockIdx.x % 8;
+  const int su = a.split_count[ug];
+  if (su <= 1) return;
+  const int grp = (int)(ug % ngroups);
+  const long long t = ug / ngroups;
+  const int l = (int)(t % a.L), item = (int)(t / a.L);
+  const int rb = item / qh, qoff = (item % qh) * kMapRows + 8 * z;
+  const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, a.B, rb);
+  const int heads_here = min(8, a.Hr - 8 * grp);
+  constexpr int PER = kMapRows * 8 * D;          // floats of one split's partial
+  const float* __restrict__ src = a.partial + (size_t)ug * a.nsplit * PER + (size_t)8 * z * 8 * D;
+  bf16* __restrict__ obase = reinterpret_cast<bf16*>(a.o) + (size_t)l * a.lso;
+  for (int c = threadIdx.x; c < 8 * 8 * D / 4; c += 256) {
+    const int idx = 4 * c;
+    const int row = idx / (8 * D), hd = (idx / D) % 8, d0 = idx % D;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src + idx);
+    for (int s2 = 1; s2 < su; ++s2) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)s2 * PER + idx);
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+    }
+    if (qoff + row < ri.rows && hd < heads_here) {
+      bf16x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = (bf16)acc[i];
+      *reinterpret_cast<bf16x4*>(obase + ((size_t)(ri.q0 + qoff + row) * a.Hr + 8 * grp + hd) * D + d0) = o4;
+    }
+  }
+}
+
 }  // namespace
 
 // The MFMA kernel's plan for these shapes (false: the portable kernel runs)
@@ -921,6 +1012,48 @@ int launch_mapped(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fas
     }
   }
   return dt == MF_BF16 ? launch_gd<bf16>(a, stream) : launch_gd<float>(a, stream);
+}
+
+// Union splits for a launch too small to fill the chip: enough that the
+// launch has about kSplitTarget workgroups, at most 8 per unit (a unit takes
+// fewer when its heads keep few blocks).  One receiver, MFMA kernel only.
+constexpr long long kSplitTarget = 1024;
+
+int mapped_splits(const MappedArgs& a, mf_dtype dt, bool allow_fast, size_t lds_limit) {
+  if (a.b.total_rb == 0 || a.L == 0 || a.nrecv != 1) return 1;
+  int kvc = 0, ns = 0, nvb = 0;
+  if (!mapped_mfma_plan(a, dt, allow_fast, lds_limit, &kvc, &ns, &nvb)) return 1;
+  const long long wg = (long long)a.b.total_rb * (a.B / kMapRows) * a.L * ((a.Hr + 7) / 8);
+  const long long s = (kSplitTarget + wg - 1) / wg;
+  return (int)(s < 1 ? 1 : (s > 8 ? 8 : s));
+}
+
+size_t mapped_split_workspace_bytes(const MappedArgs& a, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t ug = (size_t)a.b.total_rb * (a.B / kMapRows) * a.L * ((a.Hr + 7) / 8);
+  return (ug * 4 + 255) / 256 * 256 + ug * nsplit * (size_t)kMapRows * 8 * a.d * 4;
+}
+
+int launch_mapped_split(MappedArgs a, mf_dtype dt, void* ws, void* stream, bool allow_fast, size_t lds_limit) {
+  const int ns = mapped_splits(a, dt, allow_fast, lds_limit);
+  if (ns <= 1) {
+    a.nsplit = 0;
+    return launch_mapped(a, dt, stream, allow_fast, lds_limit);
+  }
+  const size_t ug = (size_t)a.b.total_rb * (a.B / kMapRows) * a.L * ((a.Hr + 7) / 8);
+  a.nsplit = ns;
+  a.split_count = reinterpret_cast<int32_t*>(ws);
+  a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (ug * 4 + 255) / 256 * 256);
+  int e = launch_mapped(a, dt, stream, allow_fast, lds_limit);
+  if (e) return e;
+  const int ngroups = (a.Hr + 7) / 8;
+  if (a.d == 128)
+    hipLaunchKernelGGL(mapped_split_reduce_kernel<128>, dim3((unsigned)(ug * 8)), dim3(256), 0, (hipStream_t)stream, a,
+                       ngroups, a.B / kMapRows);
+  else
+    hipLaunchKernelGGL(mapped_split_reduce_kernel<64>, dim3((unsigned)(ug * 8)), dim3(256), 0, (hipStream_t)stream, a,
+                       ngroups, a.B / kMapRows);
+  return (int)hipGetLastError();
 }
 
 int launch_mapped_multi(const MappedArgs& a, mf_dtype dt, void* stream, bool allow_fast, size_t lds_limit) {

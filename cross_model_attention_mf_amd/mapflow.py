@@ -27,7 +27,8 @@ EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_map_cache_destroy", "mf_map_cache_insert", "mf_map_cache_lookup", "mf_map_cache_release",
            "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_headmix_workspace_size", "mf_headmix_gram",
            "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version",
-           "mf_debug_force_portable", "mf_compress_blocks_noalloc")
+           "mf_debug_force_portable", "mf_compress_blocks_noalloc", "mf_mapped_split_workspace_size",
+           "mf_mapped_attn_v_split")
 # stages mf_debug_force_portable can send to their portable twins
 FORCE_PORTABLE = {"stats": 0x1, "select": 0x2, "extract": 0x4, "mapped": 0x8}
 
@@ -123,6 +124,10 @@ def lib():
     L.mf_mapped_attn_v_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(ReceiverDesc)), ctypes.c_int,
                                          ctypes.POINTER(BatchC), vp, vp, vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    L.mf_mapped_split_workspace_size.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC)]
+    L.mf_mapped_split_workspace_size.restype = sz
+    L.mf_mapped_attn_v_split.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
+                                         vp, vp, vp, sz, vp]
     u64p = ctypes.POINTER(ctypes.c_uint64)
     L.mf_prefix_block_hashes.argtypes = [_i32p, i64, i32, ctypes.c_uint64, u64p]
     L.mf_prefix_block_hashes.restype = i64
@@ -143,6 +148,7 @@ def lib():
                                   vp, vp, vp, sz, vp]
     L.mf_headmix_solve.argtypes = [ctypes.POINTER(HeadmixDesc), vp, vp, ctypes.c_double, vp, vp, vp]
     for f in ("mf_plan", "mf_block_stats", "mf_compress_blocks", "mf_mapped_attn_v", "mf_mapped_attn_v_multi",
+              "mf_mapped_attn_v_split",
               "mf_map_cache_create", "mf_map_cache_insert", "mf_map_cache_splice", "mf_map_cache_get_stats",
               "mf_headmix_gram", "mf_headmix_solve"):
         getattr(L, f).restype = ctypes.c_int
@@ -319,6 +325,18 @@ def mapped_attn_v(desc: ReceiverDesc, batch: Batch, row_ptr, col_idx, values, W,
     _check(lib().mf_mapped_attn_v(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(row_ptr),
                                   _ptr(col_idx), _ptr(values), _ptr(W), _ptr(v), _ptr(o),
                                   _stream(stream)))
+
+
+def mapped_split_workspace_size(desc: ReceiverDesc, batch: Batch) -> int:
+    return int(lib().mf_mapped_split_workspace_size(ctypes.byref(desc), ctypes.byref(batch.c)))
+
+
+def mapped_attn_v_split(desc: ReceiverDesc, batch: Batch, row_ptr, col_idx, values, W, v, o, workspace,
+                        stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mf_mapped_attn_v_split(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(row_ptr),
+                                        _ptr(col_idx), _ptr(values), _ptr(W), _ptr(v), _ptr(o),
+                                        _ptr(workspace), ws, _stream(stream)))
 
 
 def mapped_attn_v_multi(descs: Sequence[ReceiverDesc], batch: Batch, row_ptr, col_idx, values,

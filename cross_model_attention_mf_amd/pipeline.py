@@ -74,10 +74,12 @@ def compress(st: SenderState, q, k, tau: float, sync_count: bool = True, stream=
 
 def mapped(st: SenderState, W: torch.Tensor, v: torch.Tensor, layer_map: Sequence[int],
            out: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
-           page_size: int = 0, stream=None) -> torch.Tensor:
+           page_size: int = 0, stream=None, split: bool = False,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """W [L_r, H_r, H_s] fp32; v [L_r, Tk, H_kv_r, d] (or a paged pool
     [L_r, pages, page_size, H_kv_r, d] with block_table [S, max_pages]).
-    Returns O [L_r, Tq, H_r, d]."""
+    Returns O [L_r, Tq, H_r, d].  split=True takes mf_mapped_attn_v_split,
+    with `workspace` (allocated here when None and one is needed)."""
     if W.dim() == 2:
         W = W[None]
     if v.dim() == (4 if block_table is not None else 3):
@@ -89,8 +91,20 @@ def mapped(st: SenderState, W: torch.Tensor, v: torch.Tensor, layer_map: Sequenc
         out = torch.empty((L_r, Tq, H_r, d), dtype=v.dtype, device=v.device)
     desc = mf.receiver_desc(v, H_s, H_r, d, st.B, layer_map, st.desc.num_layers, out[0].numel(),
                             st.col_idx.numel(), block_table, page_size)
-    mf.mapped_attn_v(desc, st.batch, st.row_ptr, st.col_idx, st.values, W, v, out, stream)
+    if split:
+        if workspace is None:
+            workspace = split_workspace(desc, st.batch, v.device)
+        mf.mapped_attn_v_split(desc, st.batch, st.row_ptr, st.col_idx, st.values, W, v, out, workspace, stream)
+    else:
+        mf.mapped_attn_v(desc, st.batch, st.row_ptr, st.col_idx, st.values, W, v, out, stream)
     return out
+
+
+def split_workspace(desc, batch, device) -> Optional[torch.Tensor]:
+    """Workspace of mf_mapped_attn_v_split for this receiver and batch (None
+    when no split applies); torch's allocations are 256-byte aligned."""
+    n = mf.mapped_split_workspace_size(desc, batch)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def mapped_multi(st: SenderState, receivers: Sequence[tuple], layer_map: Sequence[int], stream=None):

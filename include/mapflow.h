@@ -253,6 +253,30 @@ mf_status mf_mapped_attn_v(const mf_receiver_desc* desc, const mf_batch* batch,
                            const void* values, const float* W, const void* v,
                            void* o, void* stream);
 
+/* mf_mapped_attn_v for launches too small to fill the GPU (few row-blocks
+ * and layers, such as a single 4K layer), where the time is that of the
+ * longest row-block's walk over its union of kept blocks.  Same arguments
+ * and output as mf_mapped_attn_v (paragraph "第三": the output is a sum over
+ * the kept blocks, with no renormalisation), plus a workspace: the union of a
+ * long row-block is cut into up to 8 column ranges walked by separate
+ * workgroups, each writing an fp32 partial output, and a second kernel sums
+ * the partials in range order into O.  O therefore equals mf_mapped_attn_v's
+ * up to fp32 summation order (the same tolerance against the definition),
+ * and repeated calls give the same bits.  When the launch is large enough,
+ * or the shape runs on the portable kernel, no split is made, the workspace
+ * is not touched and the result is mf_mapped_attn_v's bit for bit.
+ *   workspace  DEVICE, 256-byte aligned, at least
+ *              mf_mapped_split_workspace_size() bytes (may be NULL when that
+ *              is 0); calls that overlap in time need distinct workspaces
+ * Errors: as mf_mapped_attn_v, plus MF_ERR_WORKSPACE (missing or too small)
+ * and MF_ERR_INVALID (misaligned workspace). */
+size_t mf_mapped_split_workspace_size(const mf_receiver_desc* desc, const mf_batch* batch);
+mf_status mf_mapped_attn_v_split(const mf_receiver_desc* desc, const mf_batch* batch,
+                                 const int32_t* row_ptr, const int32_t* col_idx,
+                                 const void* values, const float* W, const void* v,
+                                 void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 #define MF_MAX_RECEIVERS 4
 
 /* Several receivers reuse one sender state in one launch (one sender state

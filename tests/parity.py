@@ -51,16 +51,18 @@ class GpuRun:
     outs: List[torch.Tensor]            # one O [L, Tq, H_r, d] per receiver
     block_table: Optional[np.ndarray]
     layer_map: List[int]
+    split_ws: Optional[torch.Tensor] = None   # workspace of the split launch (split=True)
 
 
 def run_gpu(wl: synth.Workload, tau: float, layers: Sequence[int], step: int = 0,
             layer_map: Optional[Sequence[int]] = None, streams: bool = False,
-            multi: bool = False,
+            multi: bool = False, split: bool = False,
             edit: Optional[Callable[[List[synth.LayerInputs]], None]] = None) -> GpuRun:
     """streams: one launch per receiver, each on its own stream; multi: every
-    receiver in one mf_mapped_attn_v_multi call; edit: changes the host
-    inputs in place before they are uploaded (the oracle checks then see the
-    edited ones)."""
+    receiver in one mf_mapped_attn_v_multi call; split: the first receiver
+    through mf_mapped_attn_v_split (its workspace is kept on the run); edit:
+    changes the host inputs in place before they are uploaded (the oracle
+    checks then see the edited ones)."""
     lay = synth.batch_layout(wl, step)
     inputs = [synth.layer_inputs(wl, l, step, lay) for l in layers]
     if edit is not None:
@@ -104,6 +106,19 @@ def run_gpu(wl: synth.Workload, tau: float, layers: Sequence[int], step: int = 0
                 outs.append(pipeline.mapped(st, W, v, lm, block_table=bt, page_size=wl.page_size, stream=s))
         for s in ss:
             cur.wait_stream(s)
+    elif split:
+        W, v, bt = launches[0]
+        L_r, H_r = W.shape[0], W.shape[1]
+        out = torch.empty((L_r, lay.total_q, H_r, wl.d), dtype=v.dtype, device=dev)
+        desc = mf.receiver_desc(v, wl.H_s, H_r, wl.d, wl.B, lm, st.desc.num_layers, out[0].numel(),
+                                st.col_idx.numel(), bt, wl.page_size if bt is not None else 0)
+        ws = pipeline.split_workspace(desc, batch, dev)
+        if ws is not None:
+            ws.fill_(0xA5)   # stale bytes: the launch must not depend on the workspace's contents
+        outs.append(pipeline.mapped(st, W, v, lm, out=out, block_table=bt, page_size=wl.page_size, split=True,
+                                    workspace=ws))
+        torch.cuda.synchronize()
+        return GpuRun(wl, tau, lay, inputs, st, outs, table, lm, ws)
     else:
         for W, v, bt in launches:
             outs.append(pipeline.mapped(st, W, v, lm, block_table=bt, page_size=wl.page_size))

@@ -82,6 +82,61 @@ def test_bf16_4k_workload_sampled():
     parity.log(f"[parity] kept fraction on sampled row-blocks {frac:.3f}")
 
 
+def split_counts(run) -> np.ndarray:
+    """The splits each (unit, head group) of a split launch took, from the
+    head of its workspace."""
+    wl = run.wl
+    ug = run.state.batch.total_rowblocks * (wl.B // 64) * len(run.layer_map) * ((wl.H_r + 7) // 8)
+    return run.split_ws[: 4 * ug].view(torch.int32).cpu().numpy()
+
+
+def test_bf16_4k_workload_split_union_walk():
+    """The 4K single layer through the split launch: its longest unions are
+    cut into column ranges; the row-blocks with the most splits and a sample
+    are checked whole against the oracle."""
+    run = parity.run_gpu(W2, W2.tau, [0], split=True)
+    n = run.state.batch.total_rowblocks
+    counts = split_counts(run).reshape(n, -1)
+    assert counts.max() > 1, "the 4K layer should take union splits"
+    longest = [int(i) for i in np.argsort(-counts.max(axis=1))[:3]]
+    rbs = sorted(set(longest) | set(parity.sample_rowblocks(n, 3, seed=7)))
+    parity.log(f"[parity] splits per row-block (max over groups): {counts.max(axis=1).tolist()}")
+    parity.check_layer(run, 0, rowblocks=rbs)
+
+
+@pytest.mark.parametrize("B,d,Hs,Hr,Hkv,seqlens,paged", [
+    (64, 128, 32, 24, None, (64 * 21 + 17,), False),           # one ragged sequence
+    (64, 64, 12, 9, None, (64 * 13 + 5, 200, 64 * 6), False),    # varlen, a partial head group
+    (128, 128, 40, 16, None, (128 * 9 + 33,), False),          # 128-row blocks: both parts split
+    (64, 128, 32, 24, 8, (64 * 11 + 3, 300), True),            # paged grouped-query values
+])
+def test_split_union_walk_matches_oracle(B, d, Hs, Hr, Hkv, seqlens, paged):
+    wl = tiny_structured("bf16", workload_id=15, B=B, d=d, H_s=Hs, H_r=Hr, H_kv_r=Hkv, seqlens=seqlens,
+                         num_layers=1, paged=paged)
+    # tau = 0.99 keeps enough blocks per row-block (up to 5-13 here) for splits
+    run = parity.run_gpu(wl, 0.99, [0], split=True)
+    assert split_counts(run).max() > 1
+    parity.check_layer(run, 0)
+    # the unsplit launch: the same sums in another order
+    plain = parity.run_gpu(wl, 0.99, [0])
+    o_s, o_p = run.outs[0].float(), plain.outs[0].float()
+    assert torch.allclose(o_s, o_p, rtol=2e-2, atol=2e-2 * float(o_p.abs().max()))
+    # partials are summed in range order: repeated calls give the same bits
+    again = parity.run_gpu(wl, 0.99, [0], split=True)
+    assert torch.equal(run.outs[0], again.outs[0])
+
+
+def test_split_launch_without_splits_is_the_plain_launch():
+    """A launch large enough to fill the chip takes no splits and needs no
+    workspace: its output is mf_mapped_attn_v's bit for bit."""
+    wl = tiny_structured("bf16", workload_id=16, B=64, d=128, H_s=32, H_r=24, seqlens=(64 * 40,), num_layers=12)
+    run = parity.run_gpu(wl, 0.95, list(range(12)), split=True)
+    assert run.split_ws is None
+    plain = parity.run_gpu(wl, 0.95, list(range(12)))
+    assert torch.equal(run.outs[0], plain.outs[0])
+    parity.check_layer(run, 11, rowblocks=[0, 39])
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("tau,full_layer", [(0.95, 8), (0.90, 3), (0.99, 12)])
 def test_bf16_8k_16_layers(tau, full_layer):
