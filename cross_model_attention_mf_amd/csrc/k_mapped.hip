@@ -255,7 +255,7 @@ struct alignas(16) UnionInfo {
 };
 
 constexpr int kUnionSlots = 3;
-constexpr int kSplitBlocks = 4;   // kept blocks of a unit's longest head per union split
+constexpr int kSplitBlocks = 4;   // union blocks per split
 constexpr size_t kMapMeta = kUnionSlots * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
 constexpr int kMapWaves = 8;
 constexpr int kMapRows = 64;   // query rows per workgroup
@@ -338,6 +338,29 @@ int group_value_heads(int Hr, int Hkv) {
   return mx;
 }
 
+// First position in [lo, hi) of an ascending column list whose column is
+// >= c (hi if none): eight-way probes while more than eight entries remain,
+// so a list of n entries takes about log8(n) + 1 rounds of loads.
+__device__ __forceinline__ int64_t lower_col(const int32_t* __restrict__ col, int64_t lo, int64_t hi, int c) {
+  while (hi - lo > 8) {
+    const int64_t step = (hi - lo + 7) >> 3;
+    int k = 0;
+#pragma unroll
+    for (int t = 1; t < 8; ++t) {
+      const int64_t p = lo + t * step;
+      k += (p < hi && col[p] < c) ? 1 : 0;
+    }
+    // probes 1 .. k lie below c: the answer is in (lo + k step, lo + (k + 1) step]
+    const int64_t nhi = min(hi, lo + (k + 1) * step);
+    lo = k == 0 ? lo : lo + k * step + 1;
+    hi = nhi;
+  }
+  int below = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) below += (lo + t < hi && col[lo + t] < c) ? 1 : 0;
+  return lo + below;
+}
+
 // column of an exhausted sender head (the merge copies it instead of a
 // col_idx entry)
 __device__ const int kNoColumn = 0x7FFFFFFF;
@@ -413,30 +436,56 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       mend = min((int64_t)a.row_ptr[row + 1], a.csr_capacity);
     }
     if (nsplit > 1) {
-      // splits this unit takes: about kSplitBlocks kept blocks of its longest
-      // head per split, at most one per causal column block; split sp walks
-      // columns [sp ncand / su, (sp + 1) ncand / su) of every head's list,
-      // whose ends a binary search finds
-      int mx = lane < a.Hs ? (int)(mend - mptr) : 0;
+      // splits this unit takes: about kSplitBlocks blocks of its union per
+      // split.  The union's columns are gathered as a bitmap in LDS (the
+      // merge slot UI[1], unused until the walk starts); split sp walks the
+      // union positions [sp U / su, (sp + 1) U / su), that is the columns
+      // [c_lo, c_hi) of every head's list.
+      unsigned* ubits = reinterpret_cast<unsigned*>(UI[1].vidx);
+      const int nw = (ri.ncand + 31) >> 5;   // <= 20 words: 632 column blocks at most
+      if (lane < nw) ubits[lane] = 0u;
+      if (lane < a.Hs) {
+        for (int64_t e0 = mptr; e0 < mend; e0 += 16) {
+          int c[16];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-      const int su = max(1, min(min(nsplit, ri.ncand), (mx + kSplitBlocks - 1) / kSplitBlocks));
-      if (lane == 0) UI[0].pad = su;
-      if (sp < su && lane < a.Hs) {
-        const int clo = (int)((long long)sp * ri.ncand / su), chi = (int)((long long)(sp + 1) * ri.ncand / su);
-        int64_t lo0 = mptr, hi0 = mend, lo1 = mptr, hi1 = mend;   // first entry >= clo, >= chi
-        while (lo0 < hi0 || lo1 < hi1) {
-          if (lo0 < hi0) {
-            const int64_t m = (lo0 + hi0) >> 1;
-            if (a.col_idx[m] < clo) lo0 = m + 1; else hi0 = m;
-          }
-          if (lo1 < hi1) {
-            const int64_t m = (lo1 + hi1) >> 1;
-            if (a.col_idx[m] < chi) lo1 = m + 1; else hi1 = m;
-          }
+          for (int t = 0; t < 16; ++t) c[t] = e0 + t < mend ? a.col_idx[e0 + t] : -1;
+#pragma unroll
+          for (int t = 0; t < 16; ++t)
+            if (c[t] >= 0) atomicOr(&ubits[c[t] >> 5], 1u << (c[t] & 31));
         }
-        mptr = lo0;
-        mend = lo1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const unsigned word = lane < nw ? ubits[lane] : 0u;
+      const int pc = __popc(word);
+      int incl = pc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int U = __shfl(incl, 63, 64);
+      const int su = max(1, min(nsplit, (U + kSplitBlocks - 1) / kSplitBlocks));
+      if (lane == 0) UI[0].pad = su;
+      if (sp < su && su > 1) {
+        // column of union position k: the owning word's (k - before)-th set bit
+        auto column_at = [&](int k) {
+          const int before = incl - pc;
+          const bool mine = k >= before && k < incl;
+          int col = 0;
+          if (mine) {
+            unsigned wd = word;
+            for (int r = k - before; r > 0; --r) wd &= wd - 1u;
+            col = 32 * lane + __builtin_ctz(wd);
+          }
+          return __shfl(col, __builtin_ctzll(__ballot(mine)), 64);
+        };
+        const int clo = sp == 0 ? 0 : column_at((int)((long long)sp * U / su));
+        const int chi = sp == su - 1 ? ri.ncand : column_at((int)((long long)(sp + 1) * U / su));
+        if (lane < a.Hs) {
+          const int64_t lo = lower_col(a.col_idx, mptr, mend, clo);
+          mend = lower_col(a.col_idx, lo, mend, chi);
+          mptr = lo;
+        }
       }
     }
     if (mptr < mend) c0 = a.col_idx[mptr];
