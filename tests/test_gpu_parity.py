@@ -3,6 +3,8 @@
 Small cases compare every output; full-size workloads run in the launch
 configuration the bench times and compare sampled row-blocks (all heads),
 always including the first and the ragged last row-block."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -124,6 +126,38 @@ def test_split_union_walk_matches_oracle(B, d, Hs, Hr, Hkv, seqlens, paged):
     # partials are summed in range order: repeated calls give the same bits
     again = parity.run_gpu(wl, 0.99, [0], split=True)
     assert torch.equal(run.outs[0], again.outs[0])
+
+
+def test_split_launch_checks_its_workspace():
+    """A split launch refuses a missing, short or misaligned workspace before
+    launching anything."""
+    wl = tiny_structured("bf16", workload_id=15, B=64, d=128, H_s=32, H_r=24, seqlens=(64 * 21 + 17,),
+                         num_layers=1)
+    run = parity.run_gpu(wl, 0.99, [0], split=True)
+    ws = run.split_ws
+    assert ws is not None
+    st, dev = run.state, ws.device
+    W = run.inputs[0].w[None].to(dev)
+    v = run.inputs[0].v[None].to(dev)
+    out = torch.zeros_like(run.outs[0])
+    desc = mf.receiver_desc(v, wl.H_s, wl.H_r, wl.d, wl.B, [0], 1, out[0].numel(), st.col_idx.numel())
+    need = mf.mapped_split_workspace_size(desc, st.batch)
+    assert need == ws.numel() > 0
+
+    def call(ptr, nbytes):
+        return mf.lib().mf_mapped_attn_v_split(ctypes.byref(desc), ctypes.byref(st.batch.c), st.row_ptr.data_ptr(),
+                                               st.col_idx.data_ptr(), st.values.data_ptr(), W.data_ptr(),
+                                               v.data_ptr(), out.data_ptr(), ptr, nbytes,
+                                               torch.cuda.current_stream().cuda_stream)
+    assert call(None, 0) == mf.MF_ERR_WORKSPACE
+    assert call(ws.data_ptr(), need - 1) == mf.MF_ERR_WORKSPACE
+    big = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    assert call(big.data_ptr() + 16, need) == mf.MF_ERR_INVALID
+    torch.cuda.synchronize()
+    assert not out.any(), "a refused call must launch nothing"
+    assert call(big.data_ptr(), need) == mf.MF_OK
+    torch.cuda.synchronize()
+    assert torch.equal(out, run.outs[0])
 
 
 def test_split_launch_without_splits_is_the_plain_launch():
