@@ -128,6 +128,21 @@ def test_split_union_walk_matches_oracle(B, d, Hs, Hr, Hkv, seqlens, paged):
     assert torch.equal(run.outs[0], again.outs[0])
 
 
+def test_split_union_walk_several_layers_and_a_layer_map():
+    """Splits over two receiver layers that read the sender's layers in
+    reverse order: each (row-block, layer, head group) has its own splits and
+    partials."""
+    wl = tiny_structured("bf16", workload_id=17, B=64, d=128, H_s=32, H_r=20, seqlens=(64 * 17 + 40, 64 * 5),
+                         num_layers=2)
+    run = parity.run_gpu(wl, 0.99, [0, 1], layer_map=[1, 0], split=True)
+    assert split_counts(run).max() > 1
+    for li in (0, 1):
+        parity.check_layer(run, li)
+    plain = parity.run_gpu(wl, 0.99, [0, 1], layer_map=[1, 0])
+    o_s, o_p = run.outs[0].float(), plain.outs[0].float()
+    assert torch.allclose(o_s, o_p, rtol=2e-2, atol=2e-2 * float(o_p.abs().max()))
+
+
 def test_split_launch_checks_its_workspace():
     """A split launch refuses a missing, short or misaligned workspace before
     launching anything."""
