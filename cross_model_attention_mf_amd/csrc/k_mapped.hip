@@ -488,8 +488,37 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         }
       }
     }
+    // the union's first two blocks, merged from each head's first three
+    // columns (one round of plain loads) instead of merge()'s copies
+    int c1 = kNoColumn, c2 = kNoColumn;
     if (mptr < mend) c0 = a.col_idx[mptr];
-    curcol[lane] = c0;
+    if (mptr + 1 < mend) c1 = a.col_idx[mptr + 1];
+    if (mptr + 2 < mend) c2 = a.col_idx[mptr + 2];
+    int adv = 0;   // columns this head has given to the two blocks
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      UnionInfo* out = &UI[u];
+      const int cur = adv == 0 ? c0 : c1;
+      int jm = cur;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) jm = min(jm, __shfl_xor(jm, off, 64));
+      const bool take = (cur == jm) && (cur != kNoColumn);
+      const unsigned long long m = __ballot(take);
+      if (take) {
+        out->vidx[lane] = (int)mptr;
+        ++mptr;
+        ++adv;
+      }
+      if (lane == 0) { out->j = jm; out->mask = m; }
+      // the block's page ids (paged values); the loop's merges fetch the rest
+      if (paged && jm != kNoColumn)
+        for (int k0 = 0; k0 < B; k0 += 64) {
+          const int key = min(jm * B + k0 + lane, ri.klen - 1);
+          async_copy4(R.block_table + (size_t)ri.seq * R.max_pages + key / R.page_size,
+                      reinterpret_cast<char*>(out->page + k0));
+        }
+    }
+    curcol[lane] = adv == 0 ? c0 : (adv == 1 ? c1 : c2);
   }
   // wave 0: next block of the union and the heads that keep it; the heads'
   // next columns and the block's page ids arrive asynchronously in LDS
@@ -522,16 +551,11 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
 #pragma unroll
     for (int c = 0; c < C::MC; ++c) async_copy4(&kNoColumn, smem + C::DOFF);
   };
+  wait_vmcnt<0>();   // page ids of the first two blocks
   __syncthreads();
   // splits past the ones this unit takes have nothing to do
   const int su = nsplit > 1 ? __builtin_amdgcn_readfirstlane(UI[0].pad) : 1;
   if (sp >= su) return;
-  if (wave == 0) merge(&UI[0]);
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (wave == 0) merge(&UI[1]);
-  wait_vmcnt<0>();
-  __syncthreads();
 
   f32x16 O[2][C::NT];
 #pragma unroll
