@@ -192,6 +192,36 @@ def test_mapped_validation(layer_map, kw, status):
     assert st == status, mf.lib().mf_last_error_message()
 
 
+@pytest.mark.parametrize("layer_map,kw,status", [
+    ([0, 2], {}, mf.MF_ERR_INVALID),
+    ([0], dict(H_kv_r=2), mf.MF_ERR_INVALID),
+    ([0], dict(H_s=0), mf.MF_ERR_UNSUPPORTED),
+    ([0], dict(block_table=16, page_size=16, max_pages=1, num_pages=4), mf.MF_ERR_INVALID),
+])
+def test_mapped_split_validation(layer_map, kw, status):
+    """The split entry point validates its receiver as mf_mapped_attn_v does,
+    before looking at the workspace."""
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    r = _receiver(layer_map, **kw)
+    st = mf.lib().mf_mapped_attn_v_split(ctypes.byref(r), ctypes.byref(b), 16, 16, 16, 16, 16, 16, None, 0, None)
+    assert st == status, mf.lib().mf_last_error_message()
+
+
+def test_mapped_split_workspace_size_of_invalid_arguments_is_zero():
+    b = _host_batch([0, 256], [0, 256], None, 64)
+    lib = mf.lib()
+    assert lib.mf_mapped_split_workspace_size(None, ctypes.byref(b)) == 0
+    assert lib.mf_mapped_split_workspace_size(ctypes.byref(_receiver([0])), None) == 0
+    assert lib.mf_mapped_split_workspace_size(ctypes.byref(_receiver([0], num_layers=-1)), ctypes.byref(b)) == 0
+
+
+def test_mapped_split_empty_batch_is_a_noop():
+    b = _host_batch([0, 0], [0, 0], None, 64)
+    r = _receiver([0])
+    assert mf.lib().mf_mapped_attn_v_split(ctypes.byref(r), ctypes.byref(b), None, None, None, None, None, None,
+                                           None, 0, None) == mf.MF_OK
+
+
 def _multi(descs, ptrs=16):
     n = len(descs)
     dp = (ctypes.POINTER(mf.ReceiverDesc) * max(n, 1))(*[ctypes.pointer(d) for d in descs])
