@@ -255,7 +255,7 @@ struct alignas(16) UnionInfo {
 };
 
 constexpr int kUnionSlots = 3;
-constexpr int kSplitBlocks = 4;   // union blocks per split
+constexpr int kSplitBlocks = 4;   // kept blocks of a unit's longest head per split
 constexpr size_t kMapMeta = kUnionSlots * sizeof(UnionInfo) + 64 * sizeof(int) + 8 * 64 * sizeof(float);
 constexpr int kMapWaves = 8;
 constexpr int kMapRows = 64;   // query rows per workgroup
@@ -435,11 +435,21 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
       mptr = min((int64_t)a.row_ptr[row], a.csr_capacity);
       mend = min((int64_t)a.row_ptr[row + 1], a.csr_capacity);
     }
+    // splits this unit takes: about kSplitBlocks kept blocks of its longest
+    // head per split (known from row_ptr alone, so the workgroups of splits
+    // past them leave after one round of loads)
+    int su = 1;
     if (nsplit > 1) {
-      // splits this unit takes: about kSplitBlocks blocks of its union per
-      // split.  The union's columns are gathered as a bitmap in LDS (the
-      // merge slot UI[1], unused until the walk starts); split sp walks the
-      // union positions [sp U / su, (sp + 1) U / su), that is the columns
+      int mx = lane < a.Hs ? (int)(mend - mptr) : 0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+      su = max(1, min(nsplit, (mx + kSplitBlocks - 1) / kSplitBlocks));
+      if (lane == 0) UI[0].pad = su;
+    }
+    if (nsplit > 1 && sp < su && su > 1) {
+      // The union's columns are gathered as a bitmap in LDS (the merge slot
+      // UI[1], unused until the walk starts); split sp walks the union
+      // positions [sp U / su, (sp + 1) U / su), that is the columns
       // [c_lo, c_hi) of every head's list.
       unsigned* ubits = reinterpret_cast<unsigned*>(UI[1].vidx);
       const int nw = (ri.ncand + 31) >> 5;   // <= 20 words: 632 column blocks at most
@@ -463,10 +473,8 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
         const int y = __shfl_up(incl, off, 64);
         if (lane >= off) incl += y;
       }
-      const int U = __shfl(incl, 63, 64);
-      const int su = max(1, min(nsplit, (U + kSplitBlocks - 1) / kSplitBlocks));
-      if (lane == 0) UI[0].pad = su;
-      if (sp < su && su > 1) {
+      const int U = __shfl(incl, 63, 64);   // >= the longest head's count, so >= su
+      {
         // column of union position k: the owning word's (k - before)-th set bit
         auto column_at = [&](int k) {
           const int before = incl - pc;
@@ -490,6 +498,7 @@ mapped_mfma_kernel(MappedArgs a, int ngroups) {
     }
     // the union's first two blocks, merged from each head's first three
     // columns (one round of plain loads) instead of merge()'s copies
+    if (sp >= su) mend = mptr;   // a split past the unit's: nothing to load
     int c1 = kNoColumn, c2 = kNoColumn;
     if (mptr < mend) c0 = a.col_idx[mptr];
     if (mptr + 1 < mend) c1 = a.col_idx[mptr + 1];
