@@ -1034,31 +1034,43 @@ int launch_gd(const MappedArgs& a, void* stream) {
 
 // Sum of a unit's split partials (in split order, so repeated calls give the
 // same bits) into its bf16 output rows.  Workgroup (unit head group ug, row
-// slice z) covers 8 query rows x 8 receiver heads x d; units that took one
-// split wrote their output themselves.
+// slice z) covers kRedRows query rows x 8 receiver heads x d: each thread
+// issues the loads of all its chunks' partials at once, then adds them.
+// Units that took one split wrote their output themselves.
+constexpr int kRedRows = 4;
 template <int D>
 __global__ void __launch_bounds__(256) mapped_split_reduce_kernel(MappedArgs a, int ngroups, int qh) {
-  const long long ug = blockIdx.x / 8;
-  const int z = blockIdx.x % 8;
+  constexpr int SL = kMapRows / kRedRows;        // row slices per unit head group
+  constexpr int NC = kRedRows * 8 * D / 4 / 256; // 16-byte chunks per thread
+  const long long ug = blockIdx.x / SL;
+  const int z = blockIdx.x % SL;
   const int su = a.split_count[ug];
   if (su <= 1) return;
   const int grp = (int)(ug % ngroups);
   const long long t = ug / ngroups;
   const int l = (int)(t % a.L), item = (int)(t / a.L);
-  const int rb = item / qh, qoff = (item % qh) * kMapRows + 8 * z;
+  const int rb = item / qh, qoff = (item % qh) * kMapRows + kRedRows * z;
   const RowBlockInfo ri = rowblock_info(a.b.plan, a.b.num_seqs, a.b.cu_q, a.b.cu_k, a.b.q_pos0, a.B, rb);
   const int heads_here = min(8, a.Hr - 8 * grp);
   constexpr int PER = kMapRows * 8 * D;          // floats of one split's partial
-  const float* __restrict__ src = a.partial + (size_t)ug * a.nsplit * PER + (size_t)8 * z * 8 * D;
+  const float* __restrict__ src = a.partial + (size_t)ug * a.nsplit * PER + (size_t)kRedRows * z * 8 * D;
   bf16* __restrict__ obase = reinterpret_cast<bf16*>(a.o) + (size_t)l * a.lso;
-  for (int c = threadIdx.x; c < 8 * 8 * D / 4; c += 256) {
-    const int idx = 4 * c;
+  f32x4 v[NC][8];
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if (s2 < su) v[k][s2] = *reinterpret_cast<const f32x4*>(src + (size_t)s2 * PER + 4 * (threadIdx.x + 256 * k));
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int idx = 4 * (threadIdx.x + 256 * k);
     const int row = idx / (8 * D), hd = (idx / D) % 8, d0 = idx % D;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(src + idx);
-    for (int s2 = 1; s2 < su; ++s2) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)s2 * PER + idx);
-      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
-    }
+    f32x4 acc = v[k][0];
+#pragma unroll
+    for (int s2 = 1; s2 < 8; ++s2)
+      if (s2 < su) {
+        acc[0] += v[k][s2][0]; acc[1] += v[k][s2][1]; acc[2] += v[k][s2][2]; acc[3] += v[k][s2][3];
+      }
     if (qoff + row < ri.rows && hd < heads_here) {
       bf16x4 o4;
 #pragma unroll
@@ -1130,10 +1142,12 @@ int launch_mapped_split(MappedArgs a, mf_dtype dt, void* ws, void* stream, bool 
   if (e) return e;
   const int ngroups = (a.Hr + 7) / 8;
   if (a.d == 128)
-    hipLaunchKernelGGL(mapped_split_reduce_kernel<128>, dim3((unsigned)(ug * 8)), dim3(256), 0, (hipStream_t)stream, a,
+    hipLaunchKernelGGL(mapped_split_reduce_kernel<128>, dim3((unsigned)(ug * (kMapRows / kRedRows))), dim3(256), 0,
+                       (hipStream_t)stream, a,
                        ngroups, a.B / kMapRows);
   else
-    hipLaunchKernelGGL(mapped_split_reduce_kernel<64>, dim3((unsigned)(ug * 8)), dim3(256), 0, (hipStream_t)stream, a,
+    hipLaunchKernelGGL(mapped_split_reduce_kernel<64>, dim3((unsigned)(ug * (kMapRows / kRedRows))), dim3(256), 0,
+                       (hipStream_t)stream, a,
                        ngroups, a.B / kMapRows);
   return (int)hipGetLastError();
 }
