@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--long-context", action="store_true",
                     help="only the 32K one-sender / two-receiver workload: statistics, compression and both "
                          "receivers' fused steps, each with its roofline")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only the matrix-pipe probe: the bf16 MFMA rate sustained alone and with the "
+                         "statistics kernel's vector work beside it")
     return ap.parse_args()
 
 
@@ -647,6 +650,37 @@ def sweep_bench(steps: int, warmup: int):
         torch.cuda.empty_cache()
 
 
+def mfma_probe_bench(steps: int, warmup: int):
+    """The bf16 MFMA rate the matrix pipe sustains (mf_mfma_probe): 2 and 4
+    waves per SIMD, alone and with the statistics kernel's vector work per
+    MFMA, against the nominal dense peak."""
+    import torch
+
+    from cross_model_attention_mf_amd import mapflow as mf
+    dev = torch.device("cuda")
+    iters = 20000
+    cases = {}
+    for blocks in (512, 1024):
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        for vec in (False, True):
+            for _ in range(max(warmup, 1)):
+                mf.mfma_probe(out, blocks, iters, vec)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(steps):
+                mf.mfma_probe(out, blocks, iters, vec)
+            ev[1].record()
+            torch.cuda.synchronize()
+            sec = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+            tflops = 524288.0 * blocks * iters / sec / 1e12
+            cases[f"{blocks // 256}_waves_per_simd{'_with_vector_work' if vec else ''}"] = {
+                "ms": round(sec * 1e3, 3), "TFLOP_per_s": round(tflops, 1),
+                "frac_of_nominal": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    _emit({"metric": "bf16 MFMA rate the matrix pipe sustains (probe)", "nominal_TFLOP_per_s": MFMA_BF16_PEAK_TFLOPS,
+           "iters": iters, "results": cases, "command": f"python bench.py --mfma-probe --steps {steps}"})
+
+
 def long_context_bench(steps: int, warmup: int):
     """32K, B=128: one 40-head sender's statistics and compression, then the
     fused step of receivers of 32 and 24 heads, one launch each on two
@@ -841,6 +875,9 @@ def main():
         return
     if args.long_context:
         long_context_bench(max(args.steps, 3), args.warmup)
+        return
+    if args.mfma_probe:
+        mfma_probe_bench(max(args.steps, 3), args.warmup)
         return
 
     if args.copy_calibration:

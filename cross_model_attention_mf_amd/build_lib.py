@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmapflow.so")
 
-HIP_SOURCES = ["api.hip", "k_stats.hip", "k_compress.hip", "k_mapped.hip", "k_headmix.hip", "map_cache.hip"]
+HIP_SOURCES = ["api.hip", "k_stats.hip", "k_compress.hip", "k_mapped.hip", "k_headmix.hip", "map_cache.hip",
+               "k_probe.hip"]
 CPP_SOURCES = ["plan.cpp"]
 
 ARCH = os.environ.get("MF_OFFLOAD_ARCH", "gfx950")

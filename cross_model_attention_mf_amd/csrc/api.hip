@@ -136,6 +136,13 @@ const char* mf_last_error_message(void) { return mf::error_buffer(); }
 
 const char* mf_version(void) { return "mapflow-mi355x 0.2"; }
 
+mf_status mf_mfma_probe(float* out, int nblocks, int iters, int with_vector, void* stream) {
+  mf::clear_error();
+  if (!out || nblocks < 1 || iters < 1) return fail(MF_ERR_INVALID, "mf_mfma_probe: out NULL or nblocks, iters < 1");
+  const int e = mf::launch_mfma_probe(out, nblocks, iters, with_vector != 0, stream);
+  return e ? hip_fail(e, "mf_mfma_probe") : MF_OK;
+}
+
 uint32_t mf_debug_force_portable(uint32_t mask) {
   const uint32_t all = MF_FORCE_PORTABLE_STATS | MF_FORCE_PORTABLE_SELECT | MF_FORCE_PORTABLE_EXTRACT |
                        MF_FORCE_PORTABLE_MAPPED;

@@ -132,6 +132,9 @@ struct HeadmixArgs {
   int32_t layer_map[MF_MAX_LAYERS];
 };
 
+// The matrix-pipe probe (mf_mfma_probe).
+int launch_mfma_probe(float* out, int nblocks, int iters, bool with_vector, void* stream);
+
 // Mask of stages forced onto their portable twins (mf_debug_force_portable).
 uint32_t forced_portable();
 

@@ -28,7 +28,7 @@ EXPORTS = ("mf_plan", "mf_block_stats", "mf_block_stats_workspace_size",
            "mf_map_cache_splice", "mf_map_cache_get_stats", "mf_headmix_workspace_size", "mf_headmix_gram",
            "mf_headmix_solve", "mf_status_string", "mf_last_error_message", "mf_version",
            "mf_debug_force_portable", "mf_compress_blocks_noalloc", "mf_mapped_split_workspace_size",
-           "mf_mapped_attn_v_split")
+           "mf_mapped_attn_v_split", "mf_mfma_probe")
 # stages mf_debug_force_portable can send to their portable twins
 FORCE_PORTABLE = {"stats": 0x1, "select": 0x2, "extract": 0x4, "mapped": 0x8}
 
@@ -124,6 +124,8 @@ def lib():
     L.mf_mapped_attn_v_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(ReceiverDesc)), ctypes.c_int,
                                          ctypes.POINTER(BatchC), vp, vp, vp, ctypes.POINTER(vp),
                                          ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    L.mf_mfma_probe.argtypes = [vp, i32, i32, i32, vp]
+    L.mf_mfma_probe.restype = ctypes.c_int
     L.mf_mapped_split_workspace_size.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC)]
     L.mf_mapped_split_workspace_size.restype = sz
     L.mf_mapped_attn_v_split.argtypes = [ctypes.POINTER(ReceiverDesc), ctypes.POINTER(BatchC), vp, vp, vp, vp,
@@ -325,6 +327,10 @@ def mapped_attn_v(desc: ReceiverDesc, batch: Batch, row_ptr, col_idx, values, W,
     _check(lib().mf_mapped_attn_v(ctypes.byref(desc), ctypes.byref(batch.c), _ptr(row_ptr),
                                   _ptr(col_idx), _ptr(values), _ptr(W), _ptr(v), _ptr(o),
                                   _stream(stream)))
+
+
+def mfma_probe(out, nblocks: int, iters: int, with_vector: bool, stream=None):
+    _check(lib().mf_mfma_probe(_ptr(out), nblocks, iters, int(with_vector), _stream(stream)))
 
 
 def mapped_split_workspace_size(desc: ReceiverDesc, batch: Batch) -> int:

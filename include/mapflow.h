@@ -469,6 +469,18 @@ const char* mf_last_error_message(void);
 /* Library version, e.g. "mapflow-mi355x 0.2". */
 const char* mf_version(void);
 
+/* Matrix-pipe probe: what the bf16 MFMA pipe of this GPU sustains, to set
+ * the statistics kernel's measured rate beside a measured ceiling as well as
+ * beside the nominal peak.  Each of nblocks workgroups of 4 waves issues
+ * 4 * iters independent MFMA 32x32x16 bf16 operations per wave (32768 flop
+ * each, so 524288 * nblocks * iters flop in all); with_vector != 0 adds the
+ * vector work the statistics kernel does per MFMA (two exp2 sums, three
+ * vector instructions each).  out: DEVICE float [nblocks * 256], overwritten
+ * with values that only keep the work from being optimised away.  Time the
+ * launch on `stream`.  Errors: MF_ERR_INVALID for NULL out, nblocks or
+ * iters < 1. */
+mf_status mf_mfma_probe(float* out, int nblocks, int iters, int with_vector, void* stream);
+
 /* Cross-check hook for tests.  Every fast kernel has a portable twin that
  * computes the same results with plain code (no MFMA, no async copies).  A
  * set bit makes later calls, on every thread, take the twin of that stage;

@@ -222,6 +222,13 @@ def test_mapped_split_empty_batch_is_a_noop():
                                            None, 0, None) == mf.MF_OK
 
 
+def test_mfma_probe_rejects_bad_arguments():
+    lib = mf.lib()
+    assert lib.mf_mfma_probe(None, 4, 10, 0, None) == mf.MF_ERR_INVALID
+    assert lib.mf_mfma_probe(16, 0, 10, 0, None) == mf.MF_ERR_INVALID
+    assert lib.mf_mfma_probe(16, 4, 0, 1, None) == mf.MF_ERR_INVALID
+
+
 def _multi(descs, ptrs=16):
     n = len(descs)
     dp = (ctypes.POINTER(mf.ReceiverDesc) * max(n, 1))(*[ctypes.pointer(d) for d in descs])
