@@ -467,3 +467,11 @@ def test_compress_with_row_ptr_not_16_byte_aligned():
     assert nnz == st.nnz
     assert torch.equal(rp, st.row_ptr)
     assert torch.equal(col[:nnz], st.col_idx[:nnz]) and torch.equal(vals[:nnz], st.values[:nnz])
+
+
+def test_mfma_probe_runs_and_writes_every_output():
+    out = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    for vec in (False, True):
+        mf.mfma_probe(out, 4, 16, vec)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
