@@ -911,6 +911,21 @@ def main():
     del src_c, dst_c
     res["hbm_copy_GB_per_s"] = round(copy_gbs, 1)
     res["mapped_attn_v"]["copy_frac"] = round(res["mapped_attn_v"]["GB_per_s"] / copy_gbs, 4)
+    # the bf16 MFMA rate the matrix pipe sustains with the statistics kernel's
+    # vector work per MFMA (mf_mfma_probe), beside the nominal peak
+    probe_out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    mf.mfma_probe(probe_out, 512, 20000, True)
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    pe0.record()
+    for _ in range(3):
+        mf.mfma_probe(probe_out, 512, 20000, True)
+    pe1.record()
+    torch.cuda.synchronize()
+    mix_tflops = 524288.0 * 512 * 20000 * 3 / (pe0.elapsed_time(pe1) * 1e-3) / 1e12
+    st_r = res["rooflines"]["stats_mfma_kernel"]
+    st_r["measured_mix_ceiling_TFLOP_per_s"] = round(mix_tflops, 1)
+    st_r["frac_of_measured_mix_ceiling"] = round(st_r["achieved"] / mix_tflops, 4)
     res.update(union_stats(st, batch, cap, wl))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
