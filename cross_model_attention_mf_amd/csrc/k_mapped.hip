@@ -1141,14 +1141,9 @@ int launch_mapped_split(MappedArgs a, mf_dtype dt, void* ws, void* stream, bool 
   int e = launch_mapped(a, dt, stream, allow_fast, lds_limit);
   if (e) return e;
   const int ngroups = (a.Hr + 7) / 8;
-  if (a.d == 128)
-    hipLaunchKernelGGL(mapped_split_reduce_kernel<128>, dim3((unsigned)(ug * (kMapRows / kRedRows))), dim3(256), 0,
-                       (hipStream_t)stream, a,
-                       ngroups, a.B / kMapRows);
-  else
-    hipLaunchKernelGGL(mapped_split_reduce_kernel<64>, dim3((unsigned)(ug * (kMapRows / kRedRows))), dim3(256), 0,
-                       (hipStream_t)stream, a,
-                       ngroups, a.B / kMapRows);
+  const dim3 grid((unsigned)(ug * (kMapRows / kRedRows)));
+  auto reduce = a.d == 128 ? mapped_split_reduce_kernel<128> : mapped_split_reduce_kernel<64>;
+  hipLaunchKernelGGL(reduce, grid, dim3(256), 0, (hipStream_t)stream, a, ngroups, a.B / kMapRows);
   return (int)hipGetLastError();
 }
 
